@@ -1,0 +1,169 @@
+/*
+ * flce.h -- C ABI of the fused LM-head projection + cross-entropy library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (for H [N,D], W [V,D], targets y [N]):
+ *   Z      = H W^T                      (never stored in device memory)
+ *   lse_n  = log sum_v exp(Z_nv)
+ *   loss_n = lse_n - Z_{n, y_n}         (0 on rows with y_n == ignore_index)
+ *   dZ     = g_n (softmax(Z)_n - onehot(y_n))
+ *   dH     = dZ W,   dW = dZ^T H
+ * Definitions: Trillion Labs "Fused Linear Cross-Entropy" reading notes,
+ * section "Cross Entropy를 다시 보면" (loss and dL/dz = softmax - onehot);
+ * PyTorch 2.13 LinearCrossEntropyLoss chapter, section "먼저 수식에서 없앨 수
+ * 있는 tensor를 찾는다" (dZ, dH = dZ W, dW = dZ^T H); Cut Cross-Entropy
+ * (arXiv 2411.09009) Sec. 4, Eq. 4 (indexed matmul minus linear-log-sum-exp)
+ * and Algorithm 4 (merged backward with the optional gradient filter).
+ * ignore_index and the mean over non-ignored rows clamped to >= 1 follow the
+ * notes' section "1. Chunked Cross-Entropy".
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates device memory: the only scratch is the caller's
+ *     workspace `ws` of at least flce_workspace_bytes() bytes (256-byte
+ *     aligned).  Extra device memory of a call is therefore exactly ws_bytes.
+ *   - Layouts are row-major and contiguous: H [N,D], W [V,D], dH [N,D],
+ *     dW [V,D]; y is int64 [N]; loss_rows, lse are float [N]; loss is float [1].
+ *     H and W share one element type (desc->in_dtype); gradients are float.
+ *     H, W, dH, dW must be 16-byte aligned.
+ *   - Work is enqueued on `stream` (0 = the null stream) and runs
+ *     asynchronously; no entry point synchronises except
+ *     flce_device_status().  Outputs are overwritten, never accumulated.
+ *   - Argument errors are reported synchronously by the return code, before
+ *     anything is enqueued; outputs are then untouched.
+ *   - A target outside [0, V) that is not ignore_index is detected on the
+ *     device: its row's loss_rows entry becomes NaN, its dZ row becomes NaN
+ *     (so dH/dW carry NaN) and bit 0 of the workspace status word is set.
+ *     Every entry point clears the status word when it starts.
+ *   - Results are deterministic: no floating-point atomics, fixed reduction
+ *     orders; two calls with the same inputs give the same bits.
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+/* Return codes. */
+enum {
+  FLCE_OK = 0,
+  FLCE_E_NULL = 1,        /* a required pointer is NULL                      */
+  FLCE_E_SHAPE = 2,       /* N < 0, V < 1, D < 8, D % 8 != 0 or a size too big */
+  FLCE_E_DTYPE = 3,       /* in_dtype is not FLCE_BF16 / FLCE_F32              */
+  FLCE_E_ALIGN = 4,       /* pointer misaligned (16 B tensors, 256 B ws)       */
+  FLCE_E_WORKSPACE = 5,   /* ws_bytes < flce_workspace_bytes(), or the budget
+                             cannot hold the smallest plan                     */
+  FLCE_E_UNSUPPORTED = 6, /* reduction/flags value not supported               */
+  FLCE_E_LAUNCH = 7,      /* a kernel launch failed (HIP error)                */
+  FLCE_E_DEVICE = 8       /* a HIP runtime call other than a launch failed     */
+};
+
+enum { FLCE_BF16 = 0, FLCE_F32 = 1 };             /* element type of H and W   */
+enum { FLCE_MEAN = 0, FLCE_SUM = 1, FLCE_NONE = 2 }; /* loss reduction           */
+
+/* Bits of flce_desc.flags. */
+enum { FLCE_FLAG_PROFILE = 1u };   /* record HIP events around every launch (see
+                                      flce_profile_read); costs a little time  */
+
+typedef struct flce_desc {
+  int64_t n_rows;          /* N >= 0 token rows                                */
+  int64_t hidden;          /* D >= 8, D % 8 == 0, D < 2^20                     */
+  int64_t vocab;           /* V >= 1, V < 2^31                                 */
+  int32_t in_dtype;        /* FLCE_BF16 or FLCE_F32                            */
+  int32_t reduction;       /* FLCE_MEAN, FLCE_SUM or FLCE_NONE                 */
+  int64_t ignore_index;    /* rows with this target are ignored (-100 usual)   */
+  float filter_eps;        /* 0 = gradient filter off; CCE Sec. 4.3 uses 2^-12.
+                              A 64x64 (rows x vocab) block of softmax - onehot
+                              whose every entry (non-ignored rows) has
+                              |.| < filter_eps is dropped from dH and dW.       */
+  uint32_t flags;          /* FLCE_FLAG_* bits, others must be 0               */
+  uint64_t ws_budget_bytes;/* 0 = 64 MiB; the planner sizes its backward
+                              blocks to fit                                    */
+} flce_desc;
+
+/* Planner decisions (for reporting and host tests; no device work). */
+typedef struct flce_plan_info {
+  int64_t ws_bytes;        /* == flce_workspace_bytes()                        */
+  int32_t band_rows;       /* NS: token rows per backward band                 */
+  int32_t band_vocab;      /* VS: vocabulary rows per backward band            */
+  int32_t n_bands_rows;    /* ceil(N / NS)                                     */
+  int32_t n_bands_vocab;   /* ceil(V / VS)                                     */
+  int32_t fwd_vocab_splits;/* workgroups sharing one 256-row tile of H         */
+  int32_t fwd_workgroups;  /* forward grid size                                */
+  int32_t tile;            /* output tile edge of every contraction (256)      */
+  int32_t filter_block;    /* edge of a filter block (64)                      */
+  int64_t dz_bytes;        /* bytes of the staged dZ band inside ws            */
+} flce_plan_info;
+
+/* Exact workspace size for *d (the maximum over the three compute entry
+ * points); 0 if *d is invalid. */
+size_t flce_workspace_bytes(const flce_desc* d);
+
+/* Fills *out with the plan for *d.  Returns FLCE_OK or an argument error. */
+int flce_plan(const flce_desc* d, flce_plan_info* out);
+
+/* Forward: loss_rows [N], lse [N] (every row, ignored ones included) and,
+ * unless reduction == FLCE_NONE, loss [1] (mean or sum of loss_rows).
+ * loss may be NULL iff reduction == FLCE_NONE.  The logits are produced tile
+ * by tile in registers and reduced with an online max/sum-exp; per-(row,
+ * vocab split) partials are merged by a second pass (CCE Alg. 2 without the
+ * lock).  The target logit is picked from the same accumulators (CCE Alg. 1). */
+int flce_forward(const flce_desc* d, const void* H, const void* W, const int64_t* y,
+                 float* loss_rows, float* lse, float* loss,
+                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward: dH [N,D] and dW [V,D] (float, overwritten) from the forward's lse.
+ * dloss is a device pointer: [1] for FLCE_MEAN / FLCE_SUM, [N] for FLCE_NONE;
+ * NULL means an upstream gradient of 1.  The logits are recomputed block by
+ * block, dZ is staged in ws one band at a time (bf16 for bf16 inputs, float
+ * for float inputs) and contracted into dH and dW (CCE Alg. 4 structure). */
+int flce_backward(const flce_desc* d, const void* H, const void* W, const int64_t* y,
+                  const float* lse, const float* dloss,
+                  float* dH, float* dW,
+                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Forward then backward with an upstream gradient of 1, in one call. */
+int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const int64_t* y,
+                       float* loss_rows, float* lse, float* loss,
+                       float* dH, float* dW,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Synchronises `stream`, then reads the status word of `ws` into *out
+ * (bit 0: a target outside [0, V) that is not ignore_index). */
+int flce_device_status(const void* ws, hipStream_t stream, int32_t* out);
+
+/* Static description of a return code. */
+const char* flce_strerror(int code);
+
+/* Kernel classes reported by flce_profile_read. */
+enum {
+  FLCE_K_FWD_LSE = 0,     /* forward contraction + online max/sum-exp        */
+  FLCE_K_LSE_COMBINE = 1, /* per-row merge of partials, loss rows            */
+  FLCE_K_FINALIZE = 2,    /* scalar loss / row scale                         */
+  FLCE_K_BWD_DZ = 3,      /* logits recompute + dZ band                      */
+  FLCE_K_BWD_GRAD = 4,    /* dH += dZ W_band and dW_band (+)= dZ^T H_band    */
+  FLCE_K_AUX = 5,         /* small fills                                     */
+  FLCE_K_COUNT = 6
+};
+
+/* Launch timing recorded while desc->flags has FLCE_FLAG_PROFILE.  Each
+ * launch made under the flag is bracketed by two HIP events on the launch
+ * stream.  flce_profile_read synchronises those events and returns, for
+ * kernel class k, the number of launches and their summed duration in ms
+ * since the last flce_profile_reset. */
+int flce_profile_reset(void);
+int flce_profile_read(int kernel_class, int64_t* launches, double* total_ms);
+
+/* Library version, e.g. "flce 0.1.0 gfx950". */
+const char* flce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLCE_H */

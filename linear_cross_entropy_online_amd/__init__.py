@@ -1,0 +1,229 @@
+"""Python binding of the fused LM-head + cross-entropy HIP library (libflce.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of include/flce.h.  PyTorch supplies device memory
+and the stream.  There is no fallback path: if libflce.so is missing or a call
+fails, an exception is raised.
+
+Functions with the C ABI's names take torch tensors:
+    flce_workspace_bytes(N, D, V, ...)            -> int
+    flce_plan(N, D, V, ...)                        -> dict
+    flce_forward(H, W, y, ...)                     -> (loss, loss_rows, lse)
+    flce_backward(H, W, y, lse, dloss=None, ...)   -> (dH, dW)
+    flce_fused_fwd_bwd(H, W, y, ...)               -> (loss, loss_rows, lse, dH, dW)
+    flce_device_status(ws)                         -> int
+and ``linear_cross_entropy(H, W, y, ...)`` is an autograd function over the
+forward / backward pair.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _abi
+from ._abi import (FLCE_BF16, FLCE_F32, FLCE_FLAG_PROFILE, FLCE_K_AUX, FLCE_K_BWD_DZ,
+                   FLCE_K_BWD_GRAD, FLCE_K_COUNT, FLCE_K_FINALIZE, FLCE_K_FWD_LSE,
+                   FLCE_K_LSE_COMBINE, FLCE_MEAN, FLCE_NONE, FLCE_SUM, FlceError, lib)
+
+__all__ = ["flce_workspace_bytes", "flce_plan", "flce_forward", "flce_backward",
+           "flce_fused_fwd_bwd", "flce_device_status", "flce_profile_reset",
+           "flce_profile_read", "linear_cross_entropy", "Workspace", "FlceError", "lib",
+           "FLCE_FLAG_PROFILE", "KERNEL_CLASSES"]
+
+_RED = {"mean": FLCE_MEAN, "sum": FLCE_SUM, "none": FLCE_NONE}
+KERNEL_CLASSES = {"fwd_lse": FLCE_K_FWD_LSE, "lse_combine": FLCE_K_LSE_COMBINE,
+                  "finalize": FLCE_K_FINALIZE, "bwd_dz": FLCE_K_BWD_DZ,
+                  "bwd_grad": FLCE_K_BWD_GRAD, "aux": FLCE_K_AUX}
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return FLCE_BF16
+    if t == torch.float32:
+        return FLCE_F32
+    raise FlceError(_abi.FLCE_E_DTYPE, f"unsupported dtype {t}")
+
+
+def make_desc(N: int, D: int, V: int, dtype=torch.bfloat16, reduction: str = "mean",
+              ignore_index: int = -100, filter_eps: float = 0.0, flags: int = 0,
+              ws_budget_bytes: int = 0) -> _abi.FlceDesc:
+    d = _abi.FlceDesc()
+    d.n_rows, d.hidden, d.vocab = int(N), int(D), int(V)
+    d.in_dtype = _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    d.reduction = _RED[reduction] if isinstance(reduction, str) else int(reduction)
+    d.ignore_index = int(ignore_index)
+    d.filter_eps = float(filter_eps)
+    d.flags = int(flags)
+    d.ws_budget_bytes = int(ws_budget_bytes)
+    return d
+
+
+def flce_workspace_bytes(N, D, V, dtype=torch.bfloat16, reduction="mean", ignore_index=-100,
+                         filter_eps=0.0, ws_budget_bytes=0) -> int:
+    d = make_desc(N, D, V, dtype, reduction, ignore_index, filter_eps, 0, ws_budget_bytes)
+    return int(lib().flce_workspace_bytes(ctypes.byref(d)))
+
+
+def flce_plan(N, D, V, dtype=torch.bfloat16, reduction="mean", ignore_index=-100,
+              filter_eps=0.0, ws_budget_bytes=0) -> dict:
+    d = make_desc(N, D, V, dtype, reduction, ignore_index, filter_eps, 0, ws_budget_bytes)
+    info = _abi.FlcePlanInfo()
+    _abi.check(lib().flce_plan(ctypes.byref(d), ctypes.byref(info)))
+    return {k: getattr(info, k) for k, _ in _abi.FlcePlanInfo._fields_}
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class Workspace:
+    """A device byte buffer sized by flce_workspace_bytes (caller-owned scratch)."""
+
+    def __init__(self, nbytes: int, device):
+        self.nbytes = int(nbytes)
+        # torch's caching allocator hands out >= 512-byte aligned blocks
+        self.buf = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=device)
+
+    def ptr(self):
+        return ctypes.c_void_p(self.buf.data_ptr())
+
+
+def _check_inputs(H, W, y):
+    if not (H.is_cuda and W.is_cuda and y.is_cuda):
+        raise FlceError(_abi.FLCE_E_NULL, "H, W and y must be device tensors")
+    if H.dtype != W.dtype:
+        raise FlceError(_abi.FLCE_E_DTYPE, "H and W must share one dtype")
+    if y.dtype != torch.int64:
+        raise FlceError(_abi.FLCE_E_DTYPE, "targets must be int64")
+    if H.dim() != 2 or W.dim() != 2 or y.dim() != 1 or H.shape[1] != W.shape[1] \
+            or y.shape[0] != H.shape[0]:
+        raise FlceError(_abi.FLCE_E_SHAPE, f"shapes H{tuple(H.shape)} W{tuple(W.shape)} "
+                                           f"y{tuple(y.shape)}")
+    if not (H.is_contiguous() and W.is_contiguous() and y.is_contiguous()):
+        raise FlceError(_abi.FLCE_E_SHAPE, "H, W and y must be contiguous")
+
+
+def _ws_for(d, device, ws):
+    need = int(lib().flce_workspace_bytes(ctypes.byref(d)))
+    if need == 0:
+        _abi.check(lib().flce_plan(ctypes.byref(d), ctypes.byref(_abi.FlcePlanInfo())))
+    if ws is None:
+        ws = Workspace(need, device)
+    return ws
+
+
+def flce_forward(H, W, y, reduction="mean", ignore_index=-100, filter_eps=0.0, flags=0,
+                 ws: Workspace | None = None, ws_budget_bytes=0, out=None):
+    """Returns (loss [1] or None, loss_rows [N], lse [N]) as float32 device tensors."""
+    _check_inputs(H, W, y)
+    N, D = H.shape
+    V = W.shape[0]
+    d = make_desc(N, D, V, H.dtype, reduction, ignore_index, filter_eps, flags, ws_budget_bytes)
+    ws = _ws_for(d, H.device, ws)
+    if out is None:
+        loss = None if reduction == "none" else torch.empty(1, dtype=torch.float32, device=H.device)
+        loss_rows = torch.empty(N, dtype=torch.float32, device=H.device)
+        lse = torch.empty(N, dtype=torch.float32, device=H.device)
+    else:
+        loss, loss_rows, lse = out
+    _abi.check(lib().flce_forward(ctypes.byref(d), _ptr(H), _ptr(W), _ptr(y), _ptr(loss_rows),
+                                  _ptr(lse), _ptr(loss), ws.ptr(), ctypes.c_size_t(ws.nbytes),
+                                  _stream(H.device)))
+    return loss, loss_rows, lse
+
+
+def flce_backward(H, W, y, lse, dloss=None, reduction="mean", ignore_index=-100, filter_eps=0.0,
+                  flags=0, ws: Workspace | None = None, ws_budget_bytes=0, out=None):
+    """Returns (dH [N,D], dW [V,D]) float32.  dloss: device float32 [1] (mean/sum) or
+    [N] (none), or None for an upstream gradient of 1."""
+    _check_inputs(H, W, y)
+    N, D = H.shape
+    V = W.shape[0]
+    d = make_desc(N, D, V, H.dtype, reduction, ignore_index, filter_eps, flags, ws_budget_bytes)
+    ws = _ws_for(d, H.device, ws)
+    if dloss is not None:
+        dloss = dloss.to(device=H.device, dtype=torch.float32).contiguous()
+        need = N if reduction == "none" else 1
+        if dloss.numel() != need:
+            raise FlceError(_abi.FLCE_E_SHAPE, f"dloss must have {need} elements")
+    if out is None:
+        dH = torch.empty(N, D, dtype=torch.float32, device=H.device)
+        dW = torch.empty(V, D, dtype=torch.float32, device=H.device)
+    else:
+        dH, dW = out
+    _abi.check(lib().flce_backward(ctypes.byref(d), _ptr(H), _ptr(W), _ptr(y), _ptr(lse),
+                                   _ptr(dloss), _ptr(dH), _ptr(dW), ws.ptr(),
+                                   ctypes.c_size_t(ws.nbytes), _stream(H.device)))
+    return dH, dW
+
+
+def flce_fused_fwd_bwd(H, W, y, reduction="mean", ignore_index=-100, filter_eps=0.0, flags=0,
+                       ws: Workspace | None = None, ws_budget_bytes=0, out=None):
+    """Forward + backward with upstream gradient 1.
+    Returns (loss, loss_rows, lse, dH, dW)."""
+    _check_inputs(H, W, y)
+    N, D = H.shape
+    V = W.shape[0]
+    d = make_desc(N, D, V, H.dtype, reduction, ignore_index, filter_eps, flags, ws_budget_bytes)
+    ws = _ws_for(d, H.device, ws)
+    if out is None:
+        dev = H.device
+        loss = None if reduction == "none" else torch.empty(1, dtype=torch.float32, device=dev)
+        loss_rows = torch.empty(N, dtype=torch.float32, device=dev)
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        dH = torch.empty(N, D, dtype=torch.float32, device=dev)
+        dW = torch.empty(V, D, dtype=torch.float32, device=dev)
+    else:
+        loss, loss_rows, lse, dH, dW = out
+    _abi.check(lib().flce_fused_fwd_bwd(ctypes.byref(d), _ptr(H), _ptr(W), _ptr(y),
+                                        _ptr(loss_rows), _ptr(lse), _ptr(loss), _ptr(dH),
+                                        _ptr(dW), ws.ptr(), ctypes.c_size_t(ws.nbytes),
+                                        _stream(H.device)))
+    return loss, loss_rows, lse, dH, dW
+
+
+def flce_device_status(ws: Workspace, device=None) -> int:
+    out = ctypes.c_int32(0)
+    dev = ws.buf.device if device is None else device
+    _abi.check(lib().flce_device_status(ws.ptr(), _stream(dev), ctypes.byref(out)))
+    return int(out.value)
+
+
+def flce_profile_reset():
+    _abi.check(lib().flce_profile_reset())
+
+
+def flce_profile_read(kernel_class) -> tuple[int, float]:
+    k = KERNEL_CLASSES[kernel_class] if isinstance(kernel_class, str) else int(kernel_class)
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0.0)
+    _abi.check(lib().flce_profile_read(k, ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)
+
+
+class _LinearCrossEntropy(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, H, W, y, reduction, ignore_index, filter_eps):
+        loss, loss_rows, lse = flce_forward(H, W, y, reduction, ignore_index, filter_eps)
+        ctx.save_for_backward(H, W, y, lse)
+        ctx.cfg = (reduction, ignore_index, filter_eps)
+        return loss_rows if reduction == "none" else loss.reshape(())
+
+    @staticmethod
+    def backward(ctx, g):
+        H, W, y, lse = ctx.saved_tensors
+        reduction, ignore_index, filter_eps = ctx.cfg
+        dH, dW = flce_backward(H, W, y, lse, g.reshape(-1).float(), reduction, ignore_index,
+                               filter_eps)
+        return dH.to(H.dtype), dW.to(W.dtype), None, None, None, None
+
+
+def linear_cross_entropy(H, W, y, reduction="mean", ignore_index=-100, filter_eps=0.0):
+    """loss = CE(H W^T, y) without materialising the logits (autograd-aware)."""
+    return _LinearCrossEntropy.apply(H, W, y, reduction, ignore_index, filter_eps)
+

@@ -1,0 +1,405 @@
+// flce.hip -- C ABI, planner and launch sequence of the fused LM-head +
+// cross-entropy library (declared in include/flce.h).
+//
+// Launch sequence of one fused call on the caller's stream:
+//   fwd_lse_kernel       grid = ceil(N/256) x Sv
+//   lse_combine_kernel   grid = ceil(N/256)
+//   finalize_kernel      1 block
+//   for each band of NS token rows:
+//     for each band of VS vocabulary rows:
+//       bwd_dz_kernel    grid = ceil(VS/256) x ceil(NS/256)
+//       bwd_grad_kernel  grid = ceil(NS/256) x ceil(D/256) + ceil(VS/256) x ceil(D/256)
+// dH of a token band accumulates over the vocabulary bands and dW of a
+// vocabulary band over the token bands; the first contribution stores, the
+// rest add, all in stream order, so the result is deterministic.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/flce.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr uint64_t kDefaultBudget = 64ull << 20;
+constexpr int kFilterBlock = 64;
+constexpr int kMaxBand = 4096;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+  int64_t N, D, V;
+  int dtype, es;
+  int Tn, Tv, Sv;      // forward tiles along N and V, vocabulary splits
+  int NS, VS;          // band sizes (multiples of 256)
+  int nbn, nbv;        // band counts
+  int frows, fcols;    // flag grid of a band
+  int nblk;            // combine blocks
+  size_t off_pm, off_ps, off_zy, off_bsum, off_bcnt, off_flags, off_flagsT, off_dz, total;
+};
+
+int validate(const flce_desc* d) {
+  if (!d) return FLCE_E_NULL;
+  if (d->n_rows < 0 || d->n_rows >= (int64_t(1) << 31)) return FLCE_E_SHAPE;
+  if (d->vocab < 1 || d->vocab >= (int64_t(1) << 31)) return FLCE_E_SHAPE;
+  if (d->hidden < 8 || d->hidden % 8 != 0 || d->hidden >= (int64_t(1) << 20)) return FLCE_E_SHAPE;
+  if (d->in_dtype != FLCE_BF16 && d->in_dtype != FLCE_F32) return FLCE_E_DTYPE;
+  if (d->reduction < FLCE_MEAN || d->reduction > FLCE_NONE) return FLCE_E_UNSUPPORTED;
+  if (d->flags & ~uint32_t(FLCE_FLAG_PROFILE)) return FLCE_E_UNSUPPORTED;
+  if (!(d->filter_eps >= 0.f) || !std::isfinite(d->filter_eps)) return FLCE_E_UNSUPPORTED;
+  return FLCE_OK;
+}
+
+size_t layout(Plan& p) {
+  size_t o = 256;  // Header
+  const size_t N = size_t(p.N);
+  p.off_pm = o;
+  o = align256(o + size_t(p.Sv) * N * 4);
+  p.off_ps = o;
+  o = align256(o + size_t(p.Sv) * N * 4);
+  p.off_zy = o;
+  o = align256(o + N * 4);
+  p.off_bsum = o;
+  o = align256(o + size_t(p.nblk) * 8);
+  p.off_bcnt = o;
+  o = align256(o + size_t(p.nblk) * 4);
+  p.off_flags = o;
+  o = align256(o + size_t(p.frows) * p.fcols);
+  p.off_flagsT = o;
+  o = align256(o + size_t(p.frows) * p.fcols);
+  p.off_dz = o;
+  o = align256(o + size_t(p.NS) * p.VS * p.es);
+  p.total = o;
+  return o;
+}
+
+int make_plan(const flce_desc* d, Plan& p) {
+  const int rc = validate(d);
+  if (rc) return rc;
+  p.N = d->n_rows;
+  p.D = d->hidden;
+  p.V = d->vocab;
+  p.dtype = d->in_dtype;
+  p.es = d->in_dtype == FLCE_BF16 ? 2 : 4;
+  p.Tn = int(cdiv(std::max<int64_t>(p.N, 1), flce::kTile));
+  p.Tv = int(cdiv(p.V, flce::kTile));
+  p.Sv = int(std::min<int64_t>(p.Tv, std::max<int64_t>(1, cdiv(256, p.Tn))));
+  p.nblk = int(cdiv(std::max<int64_t>(p.N, 1), 256));
+  p.NS = int(std::min<int64_t>(kMaxBand, cdiv(std::max<int64_t>(p.N, 1), 256) * 256));
+  p.VS = int(std::min<int64_t>(kMaxBand, cdiv(p.V, 256) * 256));
+  const uint64_t budget = d->ws_budget_bytes ? d->ws_budget_bytes : kDefaultBudget;
+  for (;;) {
+    p.frows = p.NS / kFilterBlock;
+    p.fcols = p.VS / kFilterBlock;
+    if (layout(p) <= budget) break;
+    if (p.NS <= 256 && p.VS <= 256) return FLCE_E_WORKSPACE;
+    if (p.VS >= p.NS) p.VS = std::max(256, (p.VS / 2 + 255) / 256 * 256);
+    else p.NS = std::max(256, (p.NS / 2 + 255) / 256 * 256);
+  }
+  p.nbn = int(cdiv(std::max<int64_t>(p.N, 1), p.NS));
+  p.nbv = int(cdiv(p.V, p.VS));
+  return FLCE_OK;
+}
+
+// ------------------------------------------------------------ profiling ----
+struct ProfRec {
+  int cls;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof_pending;
+int64_t g_prof_count[FLCE_K_COUNT];
+double g_prof_ms[FLCE_K_COUNT];
+
+template <class F>
+int launch(int cls, bool prof, hipStream_t s, F&& f) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (prof) {
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return FLCE_E_DEVICE;
+    if (hipEventRecord(a, s) != hipSuccess) return FLCE_E_DEVICE;
+  }
+  f();
+  const hipError_t e = hipGetLastError();
+  if (prof) {
+    if (hipEventRecord(b, s) != hipSuccess) return FLCE_E_DEVICE;
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    g_prof_pending.push_back({cls, a, b});
+  }
+  return e == hipSuccess ? FLCE_OK : FLCE_E_LAUNCH;
+}
+
+#define FLCE_TRY(x)            \
+  do {                         \
+    const int _rc = (x);       \
+    if (_rc != FLCE_OK) return _rc; \
+  } while (0)
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Ws {
+  flce::Header* hdr;
+  float *pm, *ps, *zy;
+  double* bsum;
+  int* bcnt;
+  uint8_t *flags, *flagsT;
+  void* dz;
+};
+
+Ws carve(const Plan& p, void* ws) {
+  char* b = static_cast<char*>(ws);
+  Ws w;
+  w.hdr = reinterpret_cast<flce::Header*>(b);
+  w.pm = reinterpret_cast<float*>(b + p.off_pm);
+  w.ps = reinterpret_cast<float*>(b + p.off_ps);
+  w.zy = reinterpret_cast<float*>(b + p.off_zy);
+  w.bsum = reinterpret_cast<double*>(b + p.off_bsum);
+  w.bcnt = reinterpret_cast<int*>(b + p.off_bcnt);
+  w.flags = reinterpret_cast<uint8_t*>(b + p.off_flags);
+  w.flagsT = reinterpret_cast<uint8_t*>(b + p.off_flagsT);
+  w.dz = b + p.off_dz;
+  return w;
+}
+
+template <typename T>
+int run_forward(const flce_desc* d, const Plan& p, const void* H, const void* W, const int64_t* y,
+                float* loss_rows, float* lse, float* loss, const Ws& w, bool prof, hipStream_t s) {
+  const int N = int(p.N), D = int(p.D), V = int(p.V);
+  FLCE_TRY(launch(FLCE_K_FWD_LSE, prof, s, [&] {
+    flce::fwd_lse_kernel<T><<<dim3(p.Tn * p.Sv), dim3(flce::kThreads), 0, s>>>(
+        static_cast<const T*>(H), static_cast<const T*>(W), y, N, D, V, d->ignore_index, p.Sv,
+        p.Tv, w.pm, w.ps, w.zy, w.hdr);
+  }));
+  FLCE_TRY(launch(FLCE_K_LSE_COMBINE, prof, s, [&] {
+    flce::lse_combine_kernel<<<dim3(p.nblk), dim3(256), 0, s>>>(
+        w.pm, w.ps, w.zy, y, N, V, p.Sv, d->ignore_index, lse, loss_rows, w.bsum, w.bcnt, w.hdr);
+  }));
+  FLCE_TRY(launch(FLCE_K_FINALIZE, prof, s, [&] {
+    flce::finalize_kernel<<<dim3(1), dim3(256), 0, s>>>(w.bsum, w.bcnt, p.nblk, d->reduction,
+                                                         loss, nullptr, w.hdr);
+  }));
+  return FLCE_OK;
+}
+
+template <typename T>
+int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, const int64_t* y,
+              const float* lse, const float* dloss_rows, float* dH, float* dW, const Ws& w,
+              bool prof, hipStream_t s) {
+  const int N = int(p.N), D = int(p.D), V = int(p.V);
+  const int Td = int(cdiv(D, flce::kTile));
+  for (int bn = 0; bn < p.nbn; ++bn) {
+    for (int bv = 0; bv < p.nbv; ++bv) {
+      flce::BandArgs band;
+      band.nb0 = bn * p.NS;
+      band.ns_cur = int(std::min<int64_t>(p.NS, p.N - band.nb0));
+      band.vb0 = bv * p.VS;
+      band.vs_cur = int(std::min<int64_t>(p.VS, p.V - band.vb0));
+      band.ldz = p.VS;
+      band.frows = p.frows;
+      band.fcols = p.fcols;
+      const int TMv = int(cdiv(band.vs_cur, flce::kTile));
+      const int TNn = int(cdiv(band.ns_cur, flce::kTile));
+      FLCE_TRY(launch(FLCE_K_BWD_DZ, prof, s, [&] {
+        flce::bwd_dz_kernel<T><<<dim3(TMv * TNn), dim3(flce::kThreads), 0, s>>>(
+            static_cast<const T*>(H), static_cast<const T*>(W), y, lse, dloss_rows, w.hdr, N, D, V,
+            d->ignore_index, d->reduction, d->filter_eps, band, TMv, TNn, static_cast<T*>(w.dz),
+            w.flags, w.flagsT);
+      }));
+      FLCE_TRY(launch(FLCE_K_BWD_GRAD, prof, s, [&] {
+        flce::bwd_grad_kernel<T><<<dim3(TNn * Td + TMv * Td), dim3(flce::kThreads), 0, s>>>(
+            static_cast<const T*>(H), static_cast<const T*>(W), static_cast<const T*>(w.dz),
+            w.flags, w.flagsT, dH, dW, N, D, V, band, TNn, TMv, Td, bv > 0 ? 1 : 0,
+            bn > 0 ? 1 : 0);
+      }));
+    }
+  }
+  return FLCE_OK;
+}
+
+int check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
+  if (!ws) return FLCE_E_NULL;
+  if (!aligned(ws, 256)) return FLCE_E_ALIGN;
+  if (ws_bytes < p.total) return FLCE_E_WORKSPACE;
+  return FLCE_OK;
+}
+
+int check_inputs(const Plan& p, const void* H, const void* W, const int64_t* y) {
+  if (!W) return FLCE_E_NULL;
+  if (p.N > 0 && (!H || !y)) return FLCE_E_NULL;
+  if (!aligned(W, 16) || (H && !aligned(H, 16)) || (y && !aligned(y, 8))) return FLCE_E_ALIGN;
+  return FLCE_OK;
+}
+
+int zero_dW(const Plan& p, float* dW, bool prof, hipStream_t s) {
+  return launch(FLCE_K_AUX, prof, s, [&] {
+    flce::fill_f32_kernel<<<dim3(1024), dim3(256), 0, s>>>(dW, p.V * p.D, 0.f);
+  });
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t flce_workspace_bytes(const flce_desc* d) {
+  Plan p;
+  if (make_plan(d, p) != FLCE_OK) return 0;
+  return p.total;
+}
+
+int flce_plan(const flce_desc* d, flce_plan_info* out) {
+  if (!out) return FLCE_E_NULL;
+  Plan p;
+  FLCE_TRY(make_plan(d, p));
+  out->ws_bytes = int64_t(p.total);
+  out->band_rows = p.NS;
+  out->band_vocab = p.VS;
+  out->n_bands_rows = p.nbn;
+  out->n_bands_vocab = p.nbv;
+  out->fwd_vocab_splits = p.Sv;
+  out->fwd_workgroups = p.Tn * p.Sv;
+  out->tile = flce::kTile;
+  out->filter_block = kFilterBlock;
+  out->dz_bytes = int64_t(p.NS) * p.VS * p.es;
+  return FLCE_OK;
+}
+
+int flce_forward(const flce_desc* d, const void* H, const void* W, const int64_t* y,
+                 float* loss_rows, float* lse, float* loss, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  Plan p;
+  FLCE_TRY(make_plan(d, p));
+  FLCE_TRY(check_inputs(p, H, W, y));
+  if (p.N > 0 && (!loss_rows || !lse)) return FLCE_E_NULL;
+  if (d->reduction != FLCE_NONE && !loss) return FLCE_E_NULL;
+  FLCE_TRY(check_ws(p, ws, ws_bytes));
+  const bool prof = d->flags & FLCE_FLAG_PROFILE;
+  const Ws w = carve(p, ws);
+  if (p.N == 0) {
+    return launch(FLCE_K_AUX, prof, stream, [&] {
+      flce::clear_status_kernel<<<1, 64, 0, stream>>>(w.hdr, d->reduction != FLCE_NONE ? loss : nullptr);
+    });
+  }
+  if (p.dtype == FLCE_BF16)
+    return run_forward<uint16_t>(d, p, H, W, y, loss_rows, lse, loss, w, prof, stream);
+  return run_forward<float>(d, p, H, W, y, loss_rows, lse, loss, w, prof, stream);
+}
+
+int flce_backward(const flce_desc* d, const void* H, const void* W, const int64_t* y,
+                  const float* lse, const float* dloss, float* dH, float* dW, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  Plan p;
+  FLCE_TRY(make_plan(d, p));
+  FLCE_TRY(check_inputs(p, H, W, y));
+  if (!dW || (p.N > 0 && (!dH || !lse))) return FLCE_E_NULL;
+  if (!aligned(dW, 16) || (dH && !aligned(dH, 16))) return FLCE_E_ALIGN;
+  FLCE_TRY(check_ws(p, ws, ws_bytes));
+  const bool prof = d->flags & FLCE_FLAG_PROFILE;
+  const Ws w = carve(p, ws);
+  if (p.N == 0) {
+    FLCE_TRY(launch(FLCE_K_AUX, prof, stream, [&] {
+      flce::clear_status_kernel<<<1, 64, 0, stream>>>(w.hdr, nullptr);
+    }));
+    return zero_dW(p, dW, prof, stream);
+  }
+  FLCE_TRY(launch(FLCE_K_FINALIZE, prof, stream, [&] {
+    flce::bwd_prep_kernel<<<dim3(1), dim3(256), 0, stream>>>(y, int(p.N), int(p.V), d->ignore_index,
+                                                             d->reduction, dloss, w.hdr);
+  }));
+  const float* drows = d->reduction == FLCE_NONE ? dloss : nullptr;
+  if (p.dtype == FLCE_BF16)
+    return run_bands<uint16_t>(d, p, H, W, y, lse, drows, dH, dW, w, prof, stream);
+  return run_bands<float>(d, p, H, W, y, lse, drows, dH, dW, w, prof, stream);
+}
+
+int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const int64_t* y,
+                       float* loss_rows, float* lse, float* loss, float* dH, float* dW, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  Plan p;
+  FLCE_TRY(make_plan(d, p));
+  FLCE_TRY(check_inputs(p, H, W, y));
+  if (p.N > 0 && (!loss_rows || !lse || !dH)) return FLCE_E_NULL;
+  if (!dW) return FLCE_E_NULL;
+  if (d->reduction != FLCE_NONE && !loss) return FLCE_E_NULL;
+  if (!aligned(dW, 16) || (dH && !aligned(dH, 16))) return FLCE_E_ALIGN;
+  FLCE_TRY(check_ws(p, ws, ws_bytes));
+  const bool prof = d->flags & FLCE_FLAG_PROFILE;
+  const Ws w = carve(p, ws);
+  if (p.N == 0) {
+    FLCE_TRY(launch(FLCE_K_AUX, prof, stream, [&] {
+      flce::clear_status_kernel<<<1, 64, 0, stream>>>(w.hdr, d->reduction != FLCE_NONE ? loss : nullptr);
+    }));
+    return zero_dW(p, dW, prof, stream);
+  }
+  if (p.dtype == FLCE_BF16) {
+    FLCE_TRY(run_forward<uint16_t>(d, p, H, W, y, loss_rows, lse, loss, w, prof, stream));
+    return run_bands<uint16_t>(d, p, H, W, y, lse, nullptr, dH, dW, w, prof, stream);
+  }
+  FLCE_TRY(run_forward<float>(d, p, H, W, y, loss_rows, lse, loss, w, prof, stream));
+  return run_bands<float>(d, p, H, W, y, lse, nullptr, dH, dW, w, prof, stream);
+}
+
+int flce_device_status(const void* ws, hipStream_t stream, int32_t* out) {
+  if (!ws || !out) return FLCE_E_NULL;
+  if (hipStreamSynchronize(stream) != hipSuccess) return FLCE_E_DEVICE;
+  int32_t v = 0;
+  if (hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return FLCE_E_DEVICE;
+  *out = v;
+  return FLCE_OK;
+}
+
+const char* flce_strerror(int code) {
+  switch (code) {
+    case FLCE_OK: return "ok";
+    case FLCE_E_NULL: return "a required pointer is NULL";
+    case FLCE_E_SHAPE: return "invalid shape (need N >= 0, V >= 1, D >= 8, D % 8 == 0)";
+    case FLCE_E_DTYPE: return "unsupported element type";
+    case FLCE_E_ALIGN: return "misaligned pointer (tensors 16 B, workspace 256 B)";
+    case FLCE_E_WORKSPACE: return "workspace too small for this problem";
+    case FLCE_E_UNSUPPORTED: return "unsupported reduction, flag or filter threshold";
+    case FLCE_E_LAUNCH: return "kernel launch failed";
+    case FLCE_E_DEVICE: return "HIP runtime call failed";
+    default: return "unknown error code";
+  }
+}
+
+int flce_profile_reset(void) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  for (auto& r : g_prof_pending) {
+    hipEventSynchronize(r.b);
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_prof_pending.clear();
+  for (int k = 0; k < FLCE_K_COUNT; ++k) {
+    g_prof_count[k] = 0;
+    g_prof_ms[k] = 0.0;
+  }
+  return FLCE_OK;
+}
+
+int flce_profile_read(int kernel_class, int64_t* launches, double* total_ms) {
+  if (kernel_class < 0 || kernel_class >= FLCE_K_COUNT) return FLCE_E_UNSUPPORTED;
+  if (!launches || !total_ms) return FLCE_E_NULL;
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  for (auto& r : g_prof_pending) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return FLCE_E_DEVICE;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return FLCE_E_DEVICE;
+    g_prof_count[r.cls] += 1;
+    g_prof_ms[r.cls] += ms;
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_prof_pending.clear();
+  *launches = g_prof_count[kernel_class];
+  *total_ms = g_prof_ms[kernel_class];
+  return FLCE_OK;
+}
+
+const char* flce_version(void) { return "flce 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -228,3 +228,50 @@ def filter_block_stats(H, W, y, lse, eps: float, block=(64, 64), rows=None,
             if not (np.abs(G[:, b:b + vb]) >= eps).any():
                 dropped += 1
     return dropped / max(total, 1)
+
+
+def filtered_block_samples(H, W, y, lse, g, eps: float, row_blocks, vocab_blocks,
+                           block=(64, 64), ignore_index: int = IGNORE_INDEX_DEFAULT):
+    """dH rows of whole row blocks and dW rows of whole vocabulary blocks under
+    the gradient filter (CCE Alg. 4 with blocks anchored at 0).  Deciding a
+    block needs every entry of it, so samples come in whole blocks; ``lse``
+    must be the oracle's own LSE for every row.  Returns (rows, dH_rows,
+    vrows, dW_rows)."""
+    H = _f64(H)
+    W = _f64(W)
+    y = _i64(y)
+    N, V = H.shape[0], W.shape[0]
+    nb, vb = block
+    lse = np.asarray(lse)
+    valid = y != ignore_index
+
+    def G_of(rows, cols):
+        Z = H[rows] @ W[cols].T
+        G = np.exp(Z - lse[rows, None])
+        G -= (y[rows, None] == cols[None, :])
+        G[~valid[rows]] = 0.0
+        return G
+
+    rows = np.concatenate([np.arange(b * nb, min(N, (b + 1) * nb)) for b in row_blocks])
+    dH = np.zeros((len(rows), H.shape[1]))
+    for k, b in enumerate(row_blocks):
+        rr = np.arange(b * nb, min(N, (b + 1) * nb))
+        G = G_of(rr, np.arange(V))
+        for c0 in range(0, V, vb):
+            blk = G[:, c0:c0 + vb]
+            if not (np.abs(blk) >= eps).any():
+                blk[...] = 0.0
+        off = sum(min(N, (bb + 1) * nb) - bb * nb for bb in row_blocks[:k])
+        dH[off:off + len(rr)] = (g[rr, None] * G) @ W
+    vrows = np.concatenate([np.arange(c * vb, min(V, (c + 1) * vb)) for c in vocab_blocks])
+    dW = np.zeros((len(vrows), H.shape[1]))
+    for k, c in enumerate(vocab_blocks):
+        cc = np.arange(c * vb, min(V, (c + 1) * vb))
+        off = sum(min(V, (x + 1) * vb) - x * vb for x in vocab_blocks[:k])
+        for r0 in range(0, N, nb):
+            rr = np.arange(r0, min(N, r0 + nb))
+            G = G_of(rr, cc)
+            if not (np.abs(G) >= eps).any():
+                continue
+            dW[off:off + len(cc)] += (g[rr, None] * G).T @ H[rr]
+    return rows, dH, vrows, dW

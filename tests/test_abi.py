@@ -1,0 +1,151 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header
+declares, validates arguments before touching the device, and plans a
+workspace within the budget."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_cross_entropy_online_amd as L
+from linear_cross_entropy_online_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flce.h")
+MiB = 1 << 20
+
+
+def _header():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def test_library_exports_every_declared_function():
+    src = re.sub(r"/\*.*?\*/", "", _header(), flags=re.S)
+    declared = set(re.findall(r"\b(flce_\w+)\s*\(", src))
+    assert declared == set(_abi.EXPORTS)
+    lib = L.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.flce_version().startswith(b"flce")
+
+
+def test_python_constants_match_header():
+    src = _header()
+    enums = dict((k, int(v)) for k, v in re.findall(r"\b(FLCE_[A-Z0-9_]+)\s*=\s*(\d+)u?", src))
+    for k, v in enums.items():
+        assert getattr(_abi, k) == v, k
+
+
+def test_struct_layout_matches_header():
+    # int64 x3, int32 x2, int64, float, uint32, uint64
+    assert ctypes.sizeof(_abi.FlceDesc) == 3 * 8 + 2 * 4 + 8 + 4 + 4 + 8
+    assert _abi.FlceDesc.ignore_index.offset == 32
+    assert _abi.FlceDesc.ws_budget_bytes.offset == 48
+    assert ctypes.sizeof(_abi.FlcePlanInfo) == 8 + 8 * 4 + 8
+
+
+def test_strerror_covers_codes():
+    for c in range(9):
+        assert L.lib().flce_strerror(c) != b"unknown error code"
+    assert L.lib().flce_strerror(99) == b"unknown error code"
+
+
+@pytest.mark.parametrize("N,D,V,code", [
+    (-1, 64, 10, _abi.FLCE_E_SHAPE), (4, 4, 10, _abi.FLCE_E_SHAPE), (4, 12, 10, _abi.FLCE_E_SHAPE),
+    (4, 64, 0, _abi.FLCE_E_SHAPE), (1 << 31, 64, 10, _abi.FLCE_E_SHAPE),
+])
+def test_invalid_shapes(N, D, V, code):
+    d = L.make_desc(N, D, V)
+    assert L.lib().flce_workspace_bytes(ctypes.byref(d)) == 0
+    info = _abi.FlcePlanInfo()
+    assert L.lib().flce_plan(ctypes.byref(d), ctypes.byref(info)) == code
+
+
+def test_invalid_dtype_reduction_flags_eps():
+    lib = L.lib()
+    info = _abi.FlcePlanInfo()
+    d = L.make_desc(8, 64, 10, dtype=7)
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_DTYPE
+    d = L.make_desc(8, 64, 10, reduction=5)
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    d = L.make_desc(8, 64, 10, flags=2)
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    d = L.make_desc(8, 64, 10, filter_eps=-1.0)
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    d = L.make_desc(8, 64, 10, filter_eps=float("nan"))
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    assert lib.flce_plan(None, ctypes.byref(info)) == _abi.FLCE_E_NULL
+    assert lib.flce_plan(ctypes.byref(d), None) == _abi.FLCE_E_NULL
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_argument_errors_return_before_any_device_work():
+    """Every error below is found on the host; the fake addresses are never
+    dereferenced (no GPU in this process)."""
+    lib = L.lib()
+    d = L.make_desc(8, 64, 10)
+    need = lib.flce_workspace_bytes(ctypes.byref(d))
+    A = 0x10000000
+    ok = [_fake(A), _fake(A), _fake(A), _fake(A), _fake(A), _fake(A)]
+    # forward: NULL W, misaligned H, short workspace, misaligned workspace, NULL loss (mean)
+    assert lib.flce_forward(ctypes.byref(d), ok[0], None, ok[2], ok[3], ok[4], ok[5], _fake(A),
+                            need, None) == _abi.FLCE_E_NULL
+    assert lib.flce_forward(ctypes.byref(d), _fake(A + 2), ok[1], ok[2], ok[3], ok[4], ok[5],
+                            _fake(A), need, None) == _abi.FLCE_E_ALIGN
+    assert lib.flce_forward(ctypes.byref(d), *ok, _fake(A), need - 1, None) == _abi.FLCE_E_WORKSPACE
+    assert lib.flce_forward(ctypes.byref(d), *ok, _fake(A + 16), need, None) == _abi.FLCE_E_ALIGN
+    assert lib.flce_forward(ctypes.byref(d), *ok[:5], None, _fake(A), need, None) == _abi.FLCE_E_NULL
+    # backward: NULL dW, misaligned dH
+    assert lib.flce_backward(ctypes.byref(d), ok[0], ok[1], ok[2], ok[3], None, ok[4], None,
+                             _fake(A), need, None) == _abi.FLCE_E_NULL
+    assert lib.flce_backward(ctypes.byref(d), ok[0], ok[1], ok[2], ok[3], None, _fake(A + 4),
+                             ok[5], _fake(A), need, None) == _abi.FLCE_E_ALIGN
+    # fused: NULL workspace
+    assert lib.flce_fused_fwd_bwd(ctypes.byref(d), *ok[:3], ok[3], ok[4], ok[5], ok[0], ok[1],
+                                  None, need, None) == _abi.FLCE_E_NULL
+    assert lib.flce_device_status(None, None, None) == _abi.FLCE_E_NULL
+
+
+@pytest.mark.parametrize("name,N,D,V,dt", [
+    ("large_vocab", 8192, 2048, 151552, "bf16"), ("long_context", 131072, 2048, 151552, "bf16"),
+    ("wide", 8192, 4096, 128256, "bf16"), ("mid", 4096, 1024, 32000, "bf16"),
+    ("tiny_f32", 256, 256, 4096, "f32")])
+def test_workspace_within_64_mib(name, N, D, V, dt):
+    import torch
+    p = L.flce_plan(N, D, V, dtype=torch.bfloat16 if dt == "bf16" else torch.float32)
+    assert p["ws_bytes"] <= 64 * MiB
+    assert p["ws_bytes"] == L.flce_workspace_bytes(N, D, V, torch.bfloat16 if dt == "bf16"
+                                                   else torch.float32)
+    assert p["band_rows"] % 256 == 0 and p["band_vocab"] % 256 == 0
+    assert p["n_bands_rows"] * p["band_rows"] >= N and p["n_bands_vocab"] * p["band_vocab"] >= V
+    assert p["fwd_vocab_splits"] * 256 <= ((V + 255) // 256) * 256
+
+
+def test_budget_shrinks_bands_and_reports_overflow():
+    big = L.flce_plan(8192, 2048, 151552)
+    small = L.flce_plan(8192, 2048, 151552, ws_budget_bytes=8 * MiB)
+    assert small["ws_bytes"] <= 8 * MiB < big["ws_bytes"]
+    assert small["band_rows"] * small["band_vocab"] < big["band_rows"] * big["band_vocab"]
+    with pytest.raises(L.FlceError) as e:
+        L.flce_plan(8192, 2048, 151552, ws_budget_bytes=64 << 10)
+    assert e.value.code == _abi.FLCE_E_WORKSPACE
+
+
+def test_extra_memory_is_bounded_by_rows_plus_tile():
+    """Workspace grows with N (per-row partials) but not with V beyond one band."""
+    a = L.flce_plan(8192, 2048, 151552)["ws_bytes"]
+    b = L.flce_plan(8192, 2048, 4 * 151552)["ws_bytes"]
+    c = L.flce_plan(131072, 2048, 151552)["ws_bytes"]
+    assert a == b
+    assert c - a < 16 * 131072 + MiB
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(_abi, "_LIB", None)
+    monkeypatch.setattr(_abi, "LIB_PATH", "/nonexistent/libflce.so")
+    with pytest.raises(ImportError):
+        _abi.lib()

@@ -1,0 +1,143 @@
+"""The workloads at their full sizes, run exactly as bench.py runs them
+(default workspace budget, one fused call), checked on samples the oracle can
+compute one by one and on properties that hold at any size."""
+import numpy as np
+import pytest
+import torch
+
+import flce_inputs as fi
+import linear_cross_entropy_online_amd as L
+from oracle import flce_oracle as O
+from tests.gpu_util import TOL, max_abs_rel, np64, rel, report
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+EPS = 2.0 ** -12
+
+
+def _sample(n, k, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(n, size=k, replace=False).tolist()) | {0, n - 1} | set(extra)
+    return np.array(sorted(s))
+
+
+def _properties(name, H, W, y, dH, dW, filtered=False):
+    """sum_v dW[v] = 0 (every row's dZ sums to zero; filter off) and
+    <dW, W> = <dH, H> (both equal sum dZ * Z)."""
+    Hd64, Wd64 = H.double(), W.double()
+    a = float((dW.double() * Wd64).sum())
+    b = float((dH.double() * Hd64).sum())
+    colsum = dW.double().sum(0)
+    scale = float(dW.double().abs().sum(0).max())
+    vals = dict(inner_rel=abs(a - b) / max(abs(a), abs(b)), colsum_rel=float(colsum.abs().max()) / scale)
+    report(name + "_props", **vals)
+    assert vals["inner_rel"] < 2e-2
+    if not filtered:
+        assert vals["colsum_rel"] < 1e-2
+    ign = (y == -100).to(dH.device)
+    assert torch.all(dH[ign] == 0)
+
+
+@pytest.fixture(scope="module")
+def large_vocab():
+    H, W, y = fi.make("large_vocab")
+    Hd, Wd, yd = H.to(DEV), W.to(DEV), y.to(DEV)
+    lse_ref = O.lse_all(H, W, row_chunk=512)          # fp64, every row (2 N D V)
+    return H, W, y, Hd, Wd, yd, lse_ref
+
+
+@pytest.mark.timeout(900)
+def test_large_vocab_full(large_vocab):
+    H, W, y, Hd, Wd, yd, lse_ref = large_vocab
+    loss, rows, lse, dH, dW = L.flce_fused_fwd_bwd(Hd, Wd, yd)
+    torch.cuda.synchronize()
+    yn = y.numpy()
+    valid = yn != -100
+    zy = np.zeros(len(yn))
+    idx = np.nonzero(valid)[0]
+    zy[idx] = np.einsum("nd,nd->n", np64(H[idx]), np64(W[yn[idx]]))
+    rows_ref = np.where(valid, lse_ref - zy, 0.0)
+    loss_ref = rows_ref.sum() / valid.sum()
+    g = O.row_scale(yn, W.shape[0], -100, "mean")
+    rs = _sample(H.shape[0], 48, 1)
+    vs = _sample(W.shape[0], 48, 2, extra=yn[idx[:8]].tolist())
+    dH_ref = O.dH_rows(H, W, y, lse_ref, g, rs)
+    dW_ref = O.dW_rows(H, W, y, lse_ref, g, vs)
+    vals = dict(loss=rel(loss.item(), loss_ref), lse=max_abs_rel(lse, lse_ref),
+                loss_rows=max_abs_rel(rows, rows_ref), dH=max_abs_rel(dH[rs], dH_ref),
+                dW=max_abs_rel(dW[vs], dW_ref))
+    report("large_vocab_full", **vals)
+    tol = TOL["bf16"]
+    assert vals["loss"] <= tol["loss"] and vals["lse"] <= tol["loss"]
+    assert vals["loss_rows"] <= tol["loss"]
+    assert vals["dH"] <= tol["grad"] and vals["dW"] <= tol["grad"]
+    _properties("large_vocab", H, W, y, dH.cpu(), dW.cpu())
+
+
+@pytest.mark.timeout(900)
+def test_large_vocab_filter(large_vocab):
+    """Filter on at 2^-12: whole 64 x 64 blocks sampled against the filtered
+    oracle; the error against the exact oracle is reported."""
+    H, W, y, Hd, Wd, yd, lse_ref = large_vocab
+    loss, rows, lse, dH, dW = L.flce_fused_fwd_bwd(Hd, Wd, yd, filter_eps=EPS)
+    yn = y.numpy()
+    g = O.row_scale(yn, W.shape[0], -100, "mean")
+    rblocks, vblocks = [0, 77, 127], [0, 1000, 2367]
+    r, dH_f, v, dW_f = O.filtered_block_samples(H, W, y, lse_ref, g, EPS, rblocks, vblocks)
+    dH_x = O.dH_rows(H, W, y, lse_ref, g, r)
+    dW_x = O.dW_rows(H, W, y, lse_ref, g, v)
+    frac = O.filter_block_stats(H, W, y, lse_ref, EPS, rows=np.arange(128))
+    vals = dict(skip_frac_first128rows=frac, dH=max_abs_rel(dH[r], dH_f), dW=max_abs_rel(dW[v], dW_f),
+                dH_vs_exact=max_abs_rel(dH[r], dH_x), dW_vs_exact=max_abs_rel(dW[v], dW_x))
+    report("large_vocab_filter", **vals)
+    assert vals["dH"] <= TOL["bf16"]["grad"] and vals["dW"] <= TOL["bf16"]["grad"]
+    assert rel(loss.item(), float(np64(L.flce_forward(Hd, Wd, yd)[0])[0])) == 0.0
+    _properties("large_vocab_filter", H, W, y, dH.cpu(), dW.cpu(), filtered=True)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["wide", "wide_peaked"])
+def test_wide_sampled(name):
+    H, W, y = fi.make(name)
+    Hd, Wd, yd = H.to(DEV), W.to(DEV), y.to(DEV)
+    loss, rows, lse, dH, dW = L.flce_fused_fwd_bwd(Hd, Wd, yd)
+    rs = _sample(H.shape[0], 64, 3)
+    ref = O.linear_cross_entropy(H[rs], W, y[rs], reduction="sum", grads=False)
+    yn = y.numpy()
+    g = O.row_scale(yn, W.shape[0], -100, "mean")
+    dH_ref = O.dH_rows(H, W, y, _lse_rows(H, W, rs), g, rs)
+    vals = dict(lse=max_abs_rel(lse[rs], ref["lse"]), loss_rows=max_abs_rel(rows[rs], ref["loss_rows"]),
+                dH=max_abs_rel(dH[rs], dH_ref))
+    report(name, **vals)
+    assert vals["lse"] <= 1e-3 and vals["loss_rows"] <= 1e-3 and vals["dH"] <= 2e-2
+    _properties(name, H, W, y, dH.cpu(), dW.cpu())
+    if name == "wide_peaked":
+        out = L.flce_fused_fwd_bwd(Hd, Wd, yd, filter_eps=EPS)
+        vals = dict(dH_filter_vs_exact=max_abs_rel(out[3][rs], dH_ref))
+        report(name + "_filter", **vals)
+        _properties(name + "_filter", H, W, y, out[3].cpu(), out[4].cpu(), filtered=True)
+
+
+def _lse_rows(H, W, rs):
+    full = np.zeros(H.shape[0])
+    full[rs] = O.lse_all(H[rs], W)
+    return full
+
+
+@pytest.mark.timeout(900)
+def test_long_context_sampled():
+    """131072 x 2048 x 151552, 10% ignored, sum: sampled rows and properties."""
+    H, W, y = fi.make("long_context")
+    Hd, Wd, yd = H.to(DEV), W.to(DEV), y.to(DEV)
+    plan = L.flce_plan(*H.shape, W.shape[0], reduction="sum")
+    assert plan["ws_bytes"] <= 64 << 20
+    loss, rows, lse, dH, dW = L.flce_fused_fwd_bwd(Hd, Wd, yd, reduction="sum")
+    rs = _sample(H.shape[0], 48, 4)
+    ref = O.linear_cross_entropy(H[rs], W, y[rs], reduction="sum")
+    vals = dict(lse=max_abs_rel(lse[rs], ref["lse"]), loss_rows=max_abs_rel(rows[rs], ref["loss_rows"]),
+                dH=max_abs_rel(dH[rs], ref["dH"]),
+                loss_vs_rowsum=rel(loss.item(), float(rows.double().sum())))
+    report("long_context", **vals)
+    assert vals["lse"] <= 1e-3 and vals["loss_rows"] <= 1e-3 and vals["dH"] <= 2e-2
+    assert vals["loss_vs_rowsum"] <= 1e-5
+    _properties("long_context", H, W, y, dH.cpu(), dW.cpu())

@@ -309,3 +309,17 @@ def test_page_figures():
     assert abs(lb - g["cce_lower_bound_gemma2b"][1]) < 0.5
     assert g["filter_eps"][1] == O.FILTER_EPS_DEFAULT == 2.0 ** -12
     assert int(g["ignore_index"][1]) == O.IGNORE_INDEX_DEFAULT == fi.IGNORE_INDEX
+
+
+def test_filtered_block_samples_match_full_filtered_oracle():
+    H, W, y = _case(20, 6, 30, seed=16, ignore_frac=0.2, sigma_w=2.5)
+    eps = 0.02
+    full = O.linear_cross_entropy(H, W, y, filter_eps=eps, filter_block=(4, 8), row_chunk=4)
+    g = O.row_scale(y, 30, -100, "mean")
+    rows, dH, vrows, dW = O.filtered_block_samples(H, W, y, full["lse"], g, eps, [1, 4], [0, 3],
+                                                   block=(4, 8))
+    assert np.allclose(dH, full["dH"][rows], rtol=1e-12, atol=1e-15)
+    assert np.allclose(dW, full["dW"][vrows], rtol=1e-12, atol=1e-15)
+    assert list(rows) == [4, 5, 6, 7, 16, 17, 18, 19] and list(vrows) == list(range(8)) + [24, 25, 26, 27, 28, 29]
+    unf = O.linear_cross_entropy(H, W, y)
+    assert not np.allclose(dW, unf["dW"][vrows], rtol=1e-9, atol=0)

@@ -162,7 +162,7 @@ def main():
         "total_mib_incl_outputs": round((plan["ws_bytes"] + 4 * (2 * N + 1 + N * D + V * D))
                                         / 2**20, 1),
         "plan": {"band_rows": NS, "band_vocab": VS, "bands": n_bands,
-                 "fwd_workgroups": plan["fwd_workgroups"]},
+                 "fwd_band_rows": plan["fwd_band_rows"], "fwd_workgroups": plan["fwd_workgroups"]},
         "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

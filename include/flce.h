@@ -94,8 +94,8 @@ typedef struct flce_plan_info {
   int32_t band_vocab;      /* VS: vocabulary rows per backward band            */
   int32_t n_bands_rows;    /* ceil(N / NS)                                     */
   int32_t n_bands_vocab;   /* ceil(V / VS)                                     */
-  int32_t fwd_vocab_splits;/* workgroups sharing one 256-row tile of H         */
-  int32_t fwd_workgroups;  /* forward grid size                                */
+  int32_t fwd_band_rows;   /* NF: token rows per forward band                  */
+  int32_t fwd_workgroups;  /* forward grid of one band (256 x 256 logits tiles) */
   int32_t tile;            /* output tile edge of every contraction (256)      */
   int32_t filter_block;    /* edge of a filter block (64)                      */
   int64_t dz_bytes;        /* bytes of the staged dZ band inside ws            */
@@ -110,10 +110,11 @@ int flce_plan(const flce_desc* d, flce_plan_info* out);
 
 /* Forward: loss_rows [N], lse [N] (every row, ignored ones included) and,
  * unless reduction == FLCE_NONE, loss [1] (mean or sum of loss_rows).
- * loss may be NULL iff reduction == FLCE_NONE.  The logits are produced tile
- * by tile in registers and reduced with an online max/sum-exp; per-(row,
- * vocab split) partials are merged by a second pass (CCE Alg. 2 without the
- * lock).  The target logit is picked from the same accumulators (CCE Alg. 1). */
+ * loss may be NULL iff reduction == FLCE_NONE.  The logits are produced one
+ * 256 x 256 tile per workgroup in registers and reduced to a per-(row,
+ * vocabulary tile) max and sum-exp; a second pass merges a row's partials in
+ * a fixed order (CCE Alg. 2 without the lock).  The target logit is picked
+ * from the same accumulators (CCE Alg. 1). */
 int flce_forward(const flce_desc* d, const void* H, const void* W, const int64_t* y,
                  float* loss_rows, float* lse, float* loss,
                  void* ws, size_t ws_bytes, hipStream_t stream);

@@ -31,7 +31,7 @@ class FlceDesc(ctypes.Structure):
 class FlcePlanInfo(ctypes.Structure):
     _fields_ = [("ws_bytes", ctypes.c_int64), ("band_rows", ctypes.c_int32),
                 ("band_vocab", ctypes.c_int32), ("n_bands_rows", ctypes.c_int32),
-                ("n_bands_vocab", ctypes.c_int32), ("fwd_vocab_splits", ctypes.c_int32),
+                ("n_bands_vocab", ctypes.c_int32), ("fwd_band_rows", ctypes.c_int32),
                 ("fwd_workgroups", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("filter_block", ctypes.c_int32), ("dz_bytes", ctypes.c_int64)]
 

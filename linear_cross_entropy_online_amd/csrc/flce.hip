@@ -2,8 +2,9 @@
 // cross-entropy library (declared in include/flce.h).
 //
 // Launch sequence of one fused call on the caller's stream:
-//   fwd_lse_kernel       grid = ceil(N/256) x Sv
-//   lse_combine_kernel   grid = ceil(N/256)
+//   for each band of NF token rows:
+//     fwd_lse_kernel     grid = ceil(V/256) x ceil(NF/256) logits tiles
+//     lse_combine_kernel grid = ceil(NF/256)
 //   finalize_kernel      1 block
 //   for each band of NS token rows:
 //     for each band of VS vocabulary rows:
@@ -35,12 +36,14 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Plan {
   int64_t N, D, V;
   int dtype, es;
-  int Tn, Tv, Sv;      // forward tiles along N and V, vocabulary splits
-  int NS, VS;          // band sizes (multiples of 256)
-  int nbn, nbv;        // band counts
-  int frows, fcols;    // flag grid of a band
+  int Tv;              // vocabulary tiles of 256
+  int NF, nbf;         // forward band rows (multiple of 256) and band count
+  int NS, VS;          // backward band sizes (multiples of 256)
+  int nbn, nbv;        // backward band counts
+  int frows, fcols;    // flag grid of a backward band
   int nblk;            // combine blocks
-  size_t off_pm, off_ps, off_zy, off_bsum, off_bcnt, off_flags, off_flagsT, off_dz, total;
+  size_t big;          // bytes shared by the forward partials and the dZ band
+  size_t off_zy, off_bsum, off_bcnt, off_flags, off_flagsT, off_big, total;
 };
 
 int validate(const flce_desc* d) {
@@ -55,13 +58,13 @@ int validate(const flce_desc* d) {
   return FLCE_OK;
 }
 
+// Workspace: Header | zy [N] | block sums | block counts | flags | flagsT | big,
+// where `big` holds either the forward partials of one band
+// (2 x Tv x NF floats) or the backward dZ band (NS x VS elements): the
+// forward's partials are consumed before the first dZ band is written.
 size_t layout(Plan& p) {
   size_t o = 256;  // Header
   const size_t N = size_t(p.N);
-  p.off_pm = o;
-  o = align256(o + size_t(p.Sv) * N * 4);
-  p.off_ps = o;
-  o = align256(o + size_t(p.Sv) * N * 4);
   p.off_zy = o;
   o = align256(o + N * 4);
   p.off_bsum = o;
@@ -72,8 +75,9 @@ size_t layout(Plan& p) {
   o = align256(o + size_t(p.frows) * p.fcols);
   p.off_flagsT = o;
   o = align256(o + size_t(p.frows) * p.fcols);
-  p.off_dz = o;
-  o = align256(o + size_t(p.NS) * p.VS * p.es);
+  p.off_big = o;
+  p.big = std::max(size_t(p.NS) * p.VS * p.es, size_t(2) * p.Tv * p.NF * 4);
+  o = align256(o + p.big);
   p.total = o;
   return o;
 }
@@ -86,21 +90,24 @@ int make_plan(const flce_desc* d, Plan& p) {
   p.V = d->vocab;
   p.dtype = d->in_dtype;
   p.es = d->in_dtype == FLCE_BF16 ? 2 : 4;
-  p.Tn = int(cdiv(std::max<int64_t>(p.N, 1), flce::kTile));
   p.Tv = int(cdiv(p.V, flce::kTile));
-  p.Sv = int(std::min<int64_t>(p.Tv, std::max<int64_t>(1, cdiv(256, p.Tn))));
-  p.nblk = int(cdiv(std::max<int64_t>(p.N, 1), 256));
-  p.NS = int(std::min<int64_t>(kMaxBand, cdiv(std::max<int64_t>(p.N, 1), 256) * 256));
+  const int64_t Npad = cdiv(std::max<int64_t>(p.N, 1), 256) * 256;
+  p.nblk = int(Npad / 256);
+  p.NS = int(std::min<int64_t>(kMaxBand, Npad));
   p.VS = int(std::min<int64_t>(kMaxBand, cdiv(p.V, 256) * 256));
   const uint64_t budget = d->ws_budget_bytes ? d->ws_budget_bytes : kDefaultBudget;
   for (;;) {
     p.frows = p.NS / kFilterBlock;
     p.fcols = p.VS / kFilterBlock;
+    // forward band: as many token rows as fit in the dZ band's bytes (>= 256)
+    const int64_t fit = int64_t(size_t(p.NS) * p.VS * p.es / (size_t(8) * p.Tv)) / 256 * 256;
+    p.NF = int(std::max<int64_t>(256, std::min<int64_t>(Npad, fit)));
     if (layout(p) <= budget) break;
     if (p.NS <= 256 && p.VS <= 256) return FLCE_E_WORKSPACE;
     if (p.VS >= p.NS) p.VS = std::max(256, (p.VS / 2 + 255) / 256 * 256);
     else p.NS = std::max(256, (p.NS / 2 + 255) / 256 * 256);
   }
+  p.nbf = int(cdiv(std::max<int64_t>(p.N, 1), p.NF));
   p.nbn = int(cdiv(std::max<int64_t>(p.N, 1), p.NS));
   p.nbv = int(cdiv(p.V, p.VS));
   return FLCE_OK;
@@ -143,7 +150,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 
 struct Ws {
   flce::Header* hdr;
-  float *pm, *ps, *zy;
+  float *pm, *zy;        // pm: forward partials, aliasing the dZ band
   double* bsum;
   int* bcnt;
   uint8_t *flags, *flagsT;
@@ -154,14 +161,13 @@ Ws carve(const Plan& p, void* ws) {
   char* b = static_cast<char*>(ws);
   Ws w;
   w.hdr = reinterpret_cast<flce::Header*>(b);
-  w.pm = reinterpret_cast<float*>(b + p.off_pm);
-  w.ps = reinterpret_cast<float*>(b + p.off_ps);
+  w.pm = reinterpret_cast<float*>(b + p.off_big);
   w.zy = reinterpret_cast<float*>(b + p.off_zy);
   w.bsum = reinterpret_cast<double*>(b + p.off_bsum);
   w.bcnt = reinterpret_cast<int*>(b + p.off_bcnt);
   w.flags = reinterpret_cast<uint8_t*>(b + p.off_flags);
   w.flagsT = reinterpret_cast<uint8_t*>(b + p.off_flagsT);
-  w.dz = b + p.off_dz;
+  w.dz = b + p.off_big;
   return w;
 }
 
@@ -169,15 +175,23 @@ template <typename T>
 int run_forward(const flce_desc* d, const Plan& p, const void* H, const void* W, const int64_t* y,
                 float* loss_rows, float* lse, float* loss, const Ws& w, bool prof, hipStream_t s) {
   const int N = int(p.N), D = int(p.D), V = int(p.V);
-  FLCE_TRY(launch(FLCE_K_FWD_LSE, prof, s, [&] {
-    flce::fwd_lse_kernel<T><<<dim3(p.Tn * p.Sv), dim3(flce::kThreads), 0, s>>>(
-        static_cast<const T*>(H), static_cast<const T*>(W), y, N, D, V, d->ignore_index, p.Sv,
-        p.Tv, w.pm, w.ps, w.zy, w.hdr);
-  }));
-  FLCE_TRY(launch(FLCE_K_LSE_COMBINE, prof, s, [&] {
-    flce::lse_combine_kernel<<<dim3(p.nblk), dim3(256), 0, s>>>(
-        w.pm, w.ps, w.zy, y, N, V, p.Sv, d->ignore_index, lse, loss_rows, w.bsum, w.bcnt, w.hdr);
-  }));
+  for (int bf = 0; bf < p.nbf; ++bf) {
+    const int nb0 = bf * p.NF;
+    const int ns = int(std::min<int64_t>(p.NF, p.N - nb0));
+    const int TNn = int(cdiv(ns, flce::kTile));
+    float* pm = w.pm;
+    float* ps = w.pm + size_t(p.Tv) * ns;
+    FLCE_TRY(launch(FLCE_K_FWD_LSE, prof, s, [&] {
+      flce::fwd_lse_kernel<T><<<dim3(p.Tv * TNn), dim3(flce::kThreads), 0, s>>>(
+          static_cast<const T*>(H), static_cast<const T*>(W), y, N, D, V, d->ignore_index, nb0,
+          ns, p.Tv, TNn, pm, ps, w.zy, w.hdr);
+    }));
+    FLCE_TRY(launch(FLCE_K_LSE_COMBINE, prof, s, [&] {
+      flce::lse_combine_kernel<<<dim3(TNn), dim3(256), 0, s>>>(
+          pm, ps, w.zy, y, N, V, p.Tv, nb0, ns, d->ignore_index, lse, loss_rows, w.bsum, w.bcnt,
+          w.hdr);
+    }));
+  }
   FLCE_TRY(launch(FLCE_K_FINALIZE, prof, s, [&] {
     flce::finalize_kernel<<<dim3(1), dim3(256), 0, s>>>(w.bsum, w.bcnt, p.nblk, d->reduction,
                                                          loss, nullptr, w.hdr);
@@ -259,8 +273,8 @@ int flce_plan(const flce_desc* d, flce_plan_info* out) {
   out->band_vocab = p.VS;
   out->n_bands_rows = p.nbn;
   out->n_bands_vocab = p.nbv;
-  out->fwd_vocab_splits = p.Sv;
-  out->fwd_workgroups = p.Tn * p.Sv;
+  out->fwd_band_rows = p.NF;
+  out->fwd_workgroups = p.Tv * int(cdiv(std::min<int64_t>(p.NF, std::max<int64_t>(p.N, 1)), 256));
   out->tile = flce::kTile;
   out->filter_block = kFilterBlock;
   out->dz_bytes = int64_t(p.NS) * p.VS * p.es;

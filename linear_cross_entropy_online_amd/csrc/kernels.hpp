@@ -35,102 +35,121 @@ struct Header {           // first 256 bytes of the workspace
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Sets rows >= V of the wave's 128-row block to `val` (block starts at vw).
+__device__ __forceinline__ void mask_rows(f32x16 (&acc)[4][4], int vw, int V, int lane, float val) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (vw + acc_row(i, r, lane) >= V)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j][r] = val;
+}
+
+// sum over this lane's 64 values of column block j of 2^(z log2e - ml)
+template <int J>
+__device__ __forceinline__ float col_expsum(const f32x16 (&acc)[4][4], float ml) {
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s4[i] += fast_exp2(fmaf(acc[i][J][r], kLog2e, -ml));
+  return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+}
+
+// acc[i][j][r] for the register holding wave-block row `rel` (0..127), where
+// rel = 32 i + 8 (r >> 2) + 4 half + (r & 3): a select tree on the bits of rel
+// (valid in the lane whose half matches (rel >> 2) & 1).
+template <int J>
+__device__ __forceinline__ float pick_row(const f32x16 (&acc)[4][4], int rel) {
+  const int i = rel >> 5, q = (rel >> 3) & 3, e = rel & 3;
+  float t[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    t[r] = i == 0 ? acc[0][J][r] : i == 1 ? acc[1][J][r] : i == 2 ? acc[2][J][r] : acc[3][J][r];
+  float u[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    u[x] = q == 0 ? t[x] : q == 1 ? t[4 + x] : q == 2 ? t[8 + x] : t[12 + x];
+  return e == 0 ? u[0] : e == 1 ? u[1] : e == 2 ? u[2] : u[3];
+}
+
+// Max and sum-exp of one 32-column block (token rows) over this lane's 64
+// logits of the tile, and the target pick.
+template <int J>
+__device__ __forceinline__ void fwd_column(const f32x16 (&acc)[4][4], float& m, float& s, int rel,
+                                           int lane, float* zy_col) {
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[i][J][r]);
+  m = tmax;
+  s = tmax == -INFINITY ? 0.f : col_expsum<J>(acc, tmax * kLog2e);
+  const bool hit = (unsigned)rel < 128u;
+  if (__any(hit)) {
+    const float z = pick_row<J>(acc, rel & 127);
+    if (hit && ((rel >> 2) & 1) == (lane >> 5)) *zy_col = z;
+  }
+}
+
 // ------------------------------------------------------------- forward ----
+// One 256 (vocabulary) x 256 (token rows) logits tile per workgroup, for the
+// token rows [nb0, nb0 + ns) of a band: Z = W_v H_n^T stays in registers; the
+// tile's per-row max m and sum s = sum_v exp(Z - m) go to
+// part_m / part_s [vocab tile][row of the band], and the target logit of a
+// row whose target lies in the tile goes to zy[row].
 template <typename T>
 __global__ void __launch_bounds__(kThreads, 1)
 fwd_lse_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* __restrict__ y,
-               int N, int D, int V, int64_t ignore, int Sv, int Tv, float* __restrict__ part_m,
-               float* __restrict__ part_s, float* __restrict__ zy, Header* __restrict__ hdr) {
+               int N, int D, int V, int64_t ignore, int nb0, int ns, int TMv, int TNn,
+               float* __restrict__ part_m, float* __restrict__ part_s, float* __restrict__ zy,
+               Header* __restrict__ hdr) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  if (nb0 == 0 && blockIdx.x == 0 && threadIdx.x == 0) hdr->status = 0;   // start of a forward
   const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int nt = t / Sv, split = t - nt * Sv;
-  const int n0 = nt * kTile;
-  const int vt0 = (int)((int64_t)split * Tv / Sv);
-  const int vt1 = (int)((int64_t)(split + 1) * Tv / Sv);
+  int tm, tn;
+  grouped_tile(t, TMv, TNn, 4, tm, tn);
+  const int v0 = tm * kTile, n0 = nb0 + tn * kTile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  if (blockIdx.x == 0 && tid == 0) hdr->status = 0;
-
-  int ytg[4];
-  float mrun[4], srun[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 128 + j * 32 + (lane & 31);
-    const int64_t yy = n < N ? y[n] : ignore;
-    ytg[j] = (yy >= 0 && yy < V) ? (int)yy : -1;
-    mrun[j] = -INFINITY;
-    srun[j] = 0.f;
-  }
   const Operand A{reinterpret_cast<const char*>(W), D, V, D};
   const Operand B{reinterpret_cast<const char*>(H), D, N, D};
   const int nk = (D + kKStep<T> - 1) / kKStep<T>;
   f32x16 acc[4][4];
+  gemm_tile<T, false, false>(A, B, v0, n0, nk, AllActive{}, acc, lds);
 
-  for (int vt = vt0; vt < vt1; ++vt) {
-    const int v0 = vt * kTile;
-    gemm_tile<T, false, false>(A, B, v0, n0, nk, AllActive{}, acc, lds);
-    const int vw = v0 + wm * 128;  // first vocabulary row of this wave's block
-    if (vw + 128 > V) {
+  const int vw = v0 + wm * 128;  // first vocabulary row of this wave's block
+  int rel[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (vw + acc_row(i, r, lane) >= V)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j][r] = -INFINITY;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[i][j][r]);
-      const float mnew = fmaxf(mrun[j], tmax);
-      if (mnew != -INFINITY) {
-        const float ml = mnew * kLog2e;
-        float s4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s4[i] += fast_exp2(fmaf(acc[i][j][r], kLog2e, -ml));
-        srun[j] = srun[j] * fast_exp2((mrun[j] - mnew) * kLog2e) + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
-        mrun[j] = mnew;
-      }
-      const int rel = ytg[j] - vw;
-      const bool hit = (unsigned)rel < 128u;
-      if (__any(hit)) {
-        float z = 0.f;
-        bool own = false;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (rel == acc_row(i, r, lane)) {
-              z = acc[i][j][r];
-              own = true;
-            }
-        if (hit && own) zy[n0 + wn * 128 + j * 32 + (lane & 31)] = z;
-      }
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn * 128 + j * 32 + (lane & 31);
+    const int64_t yy = n < N ? y[n] : ignore;
+    rel[j] = (yy >= 0 && yy < V) ? (int)(yy - vw) : -1;
   }
+  if (vw + 128 > V) mask_rows(acc, vw, V, lane, -INFINITY);   // last vocabulary tile
+  float m[4], s[4];
+  float* zc = zy + n0 + wn * 128 + (lane & 31);
+  fwd_column<0>(acc, m[0], s[0], rel[0], lane, zc);
+  fwd_column<1>(acc, m[1], s[1], rel[1], lane, zc + 32);
+  fwd_column<2>(acc, m[2], s[2], rel[2], lane, zc + 64);
+  fwd_column<3>(acc, m[3], s[3], rel[3], lane, zc + 96);
 
   // merge the two lanes holding one token column, then the two waves
   float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float mo = __shfl_xor(mrun[j], 32), so = __shfl_xor(srun[j], 32);
-    const float M = fmaxf(mrun[j], mo);
-    srun[j] = (M == -INFINITY) ? 0.f
-                               : srun[j] * fast_exp2((mrun[j] - M) * kLog2e) +
-                                     so * fast_exp2((mo - M) * kLog2e);
-    mrun[j] = M;
+    const float mo = __shfl_xor(m[j], 32), so = __shfl_xor(s[j], 32);
+    const float M = fmaxf(m[j], mo);
+    s[j] = (M == -INFINITY) ? 0.f
+                            : s[j] * fast_exp2((m[j] - M) * kLog2e) + so * fast_exp2((mo - M) * kLog2e);
+    m[j] = M;
   }
   if (wm == 1 && lane < 32) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      red[(wn * 128 + j * 32 + lane) * 2 + 0] = mrun[j];
-      red[(wn * 128 + j * 32 + lane) * 2 + 1] = srun[j];
+      red[(wn * 128 + j * 32 + lane) * 2 + 0] = m[j];
+      red[(wn * 128 + j * 32 + lane) * 2 + 1] = s[j];
     }
   }
   __syncthreads();
@@ -139,14 +158,14 @@ fwd_lse_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* 
     for (int j = 0; j < 4; ++j) {
       const int c = wn * 128 + j * 32 + lane;
       const float mo = red[c * 2 + 0], so = red[c * 2 + 1];
-      const float M = fmaxf(mrun[j], mo);
+      const float M = fmaxf(m[j], mo);
       const float S = (M == -INFINITY) ? 0.f
-                                       : srun[j] * fast_exp2((mrun[j] - M) * kLog2e) +
+                                       : s[j] * fast_exp2((m[j] - M) * kLog2e) +
                                              so * fast_exp2((mo - M) * kLog2e);
-      const int n = n0 + c;
-      if (n < N) {
-        part_m[(int64_t)split * N + n] = M;
-        part_s[(int64_t)split * N + n] = S;
+      const int nl = tn * kTile + c;   // row within the band
+      if (nl < ns) {
+        part_m[(int64_t)tm * ns + nl] = M;
+        part_s[(int64_t)tm * ns + nl] = S;
       }
     }
   }
@@ -172,21 +191,22 @@ __device__ __forceinline__ void block_reduce_256(double& s, int& c, double* sh_s
 __global__ void __launch_bounds__(256)
 lse_combine_kernel(const float* __restrict__ part_m, const float* __restrict__ part_s,
                    const float* __restrict__ zy, const int64_t* __restrict__ y, int N, int V,
-                   int Sv, int64_t ignore, float* __restrict__ lse, float* __restrict__ loss_rows,
-                   double* __restrict__ blk_sum, int* __restrict__ blk_cnt,
-                   Header* __restrict__ hdr) {
+                   int Tv, int nb0, int ns, int64_t ignore, float* __restrict__ lse,
+                   float* __restrict__ loss_rows, double* __restrict__ blk_sum,
+                   int* __restrict__ blk_cnt, Header* __restrict__ hdr) {
   __shared__ double sh_s[256];
   __shared__ int sh_c[256];
-  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int nl = blockIdx.x * 256 + threadIdx.x;   // row within the band
+  const int n = nb0 + nl;
   double s = 0.0;
   int c = 0;
-  if (n < N) {
+  if (nl < ns) {
     float M = -INFINITY;
-    for (int k = 0; k < Sv; ++k) M = fmaxf(M, part_m[(int64_t)k * N + n]);
+    for (int k = 0; k < Tv; ++k) M = fmaxf(M, part_m[(int64_t)k * ns + nl]);
     float S = 0.f;
-    for (int k = 0; k < Sv; ++k) {
-      const float m = part_m[(int64_t)k * N + n];
-      S += part_s[(int64_t)k * N + n] * fast_exp2((m - M) * kLog2e);
+    for (int k = 0; k < Tv; ++k) {
+      const float m = part_m[(int64_t)k * ns + nl];
+      S += part_s[(int64_t)k * ns + nl] * fast_exp2((m - M) * kLog2e);
     }
     const float l = M + fast_log2(S) * kLn2;
     lse[n] = l;
@@ -206,8 +226,8 @@ lse_combine_kernel(const float* __restrict__ part_m, const float* __restrict__ p
   }
   block_reduce_256(s, c, sh_s, sh_c);
   if (threadIdx.x == 0) {
-    blk_sum[blockIdx.x] = s;
-    blk_cnt[blockIdx.x] = c;
+    blk_sum[nb0 / 256 + blockIdx.x] = s;
+    blk_cnt[nb0 / 256 + blockIdx.x] = c;
   }
 }
 
@@ -313,74 +333,103 @@ bwd_dz_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* _
   gemm_tile<T, false, false>(A, B, v0, n0, nk, AllActive{}, acc, lds);
 
   float g[4], ml[4];
-  int yt[4];
-  bool valid[4], bad[4];
+  int rel[4];
+  bool bad[4];
   const float gs = hdr->gscale;
+  const int vw = v0 + wm * 128;  // first vocabulary row of this wave's block
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = n0 + wn * 128 + j * 32 + (lane & 31);
     const bool in = n < N;
     const int64_t yy = in ? y[n] : ignore;
-    valid[j] = in && yy != ignore;
-    bad[j] = valid[j] && (yy < 0 || yy >= V);
-    float gj = reduction == 2 ? (dloss_rows ? (in ? dloss_rows[n] : 0.f) : 1.f) : gs;
-    gj = valid[j] ? gj : 0.f;
-    g[j] = bad[j] ? __builtin_nanf("") : gj;
-    ml[j] = in ? lse[n] * kLog2e : 0.f;
-    yt[j] = (valid[j] && !bad[j]) ? (int)yy : -1;
+    const bool valid = in && yy != ignore;
+    bad[j] = valid && (yy < 0 || yy >= V);
+    const float gj = reduction == 2 ? (dloss_rows ? dloss_rows[in ? n : 0] : 1.f) : gs;
+    g[j] = bad[j] ? __builtin_nanf("") : (valid ? gj : 0.f);
+    ml[j] = valid ? lse[n] * kLog2e : INFINITY;       // rows outside the loss get p = 0
+    rel[j] = (valid && !bad[j]) ? (int)(yy - vw) : -1;
   }
-  const int vw = v0 + wm * 128;
-  bool keep[2][2] = {{false, false}, {false, false}};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int v = vw + acc_row(i, r, lane);
-      const bool vin = v < V;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p = fast_exp2(fmaf(acc[i][j][r], kLog2e, -ml[j]));
-        float G = p - (v == yt[j] ? 1.f : 0.f);
-        const bool ok = valid[j] && vin;
-        G = ok ? G : 0.f;
-        keep[i >> 1][j >> 1] |= ok && (fabsf(G) >= eps || bad[j]);
-        acc[i][j][r] = g[j] * G;
-      }
-    }
   const int fr0 = (n0 - band.nb0 + wn * 128) >> 6;   // flag row of this wave's first 64 rows
   const int fc0 = (v0 - band.vb0 + wm * 128) >> 6;   // flag column of its first 64 vocab rows
+  // One pair of 32-column blocks (64 token rows) at a time, so at most 128
+  // softmax values sit in VGPRs while the accumulators stay where they are.
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int bj = 0; bj < 2; ++bj) {
+    float p[2][4][16];
+    float kmax[2] = {0.f, 0.f};
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj) {
-      const bool kp = __any(keep[bi][bj]);
-      if (!kp) {
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int i = 2 * bi; i < 2 * bi + 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 2 * bj; j < 2 * bj + 2; ++j)
+        for (int r = 0; r < 16; ++r) {
+          p[jj][i][r] = fast_exp2(fmaf(acc[i][2 * bj + jj][r], kLog2e, -ml[2 * bj + jj]));
+          kmax[i >> 1] = fmaxf(kmax[i >> 1], p[jj][i][r]);
+        }
+    // rare: vocabulary rows past V (last tile) and targets (G = p - 1) change
+    // the block maxima, which are then recomputed over |G|
+    bool redo = false;
+    if (vw + 128 > V) {
+      redo = true;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (vw + acc_row(i, r, lane) >= V) p[0][i][r] = p[1][i][r] = 0.f;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int rl = rel[2 * bj + jj];
+      const bool hit = (unsigned)rl < 128u;
+      if (__any(hit)) {
+        redo = true;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (hit && rl == acc_row(i, r, lane)) p[jj][i][r] -= 1.f;
       }
+    }
+    if (redo) {
+      kmax[0] = kmax[1] = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) kmax[i >> 1] = fmaxf(kmax[i >> 1], fabsf(p[jj][i][r]));
+    }
+    // CCE Alg. 4 filter on 64x64 blocks: dropped iff every |G| < eps (an
+    // all-zero block is dropped too, which changes nothing).  Dropped blocks
+    // are written as zeros and flagged so the contractions can skip them.
+    float gk[2][2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      const bool kp = __any((kmax[bi] > 0.f && kmax[bi] >= eps) || bad[2 * bj] || bad[2 * bj + 1]);
+      gk[bi][0] = kp ? g[2 * bj] : 0.f;
+      gk[bi][1] = kp ? g[2 * bj + 1] : 0.f;
       if (lane == 0) {
         const int fr = fr0 + bj, fc = fc0 + bi;
         flags[fr * band.fcols + fc] = kp ? 0 : 1;
         flagsT[fc * band.frows + fr] = kp ? 0 : 1;
       }
     }
-  // dZ band is [rows of the band][vocab of the band], row stride ldz
+    // dZ = g (p - onehot) into the band [rows of the band][vocab], row stride ldz
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int nl = n0 - band.nb0 + wn * 128 + j * 32 + (lane & 31);
-    T* row = dz + (int64_t)nl * band.ldz + (vw - band.vb0);
+    for (int jj = 0; jj < 2; ++jj) {
+      const int nl = n0 - band.nb0 + wn * 128 + (2 * bj + jj) * 32 + (lane & 31);
+      T* row = dz + (int64_t)nl * band.ldz + (vw - band.vb0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const float gg = gk[i >> 1][jj];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = i * 32 + 8 * q + 4 * (lane >> 5);
-        store4<T>(row + c, acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                  acc[i][j][4 * q + 3]);
+        for (int q = 0; q < 4; ++q) {
+          const int c = i * 32 + 8 * q + 4 * (lane >> 5);
+          store4<T>(row + c, gg * p[jj][i][4 * q + 0], gg * p[jj][i][4 * q + 1],
+                    gg * p[jj][i][4 * q + 2], gg * p[jj][i][4 * q + 3]);
+        }
       }
+    }
   }
 }
 

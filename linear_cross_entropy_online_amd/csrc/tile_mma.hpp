@@ -5,15 +5,21 @@
 // 128x128 block of the 256x256 fp32 accumulator tile, i.e. 4x4 MFMA blocks of
 // 32x32 (v_mfma_f32_32x32x16_bf16 for bf16 inputs, v_mfma_f32_32x32x2_f32 for
 // fp32 inputs).  Operands are staged through LDS 128 bytes of K at a time per
-// tile row, double buffered (2 stages x (A + B) x 32 KiB = 128 KiB of the
-// 160 KiB LDS), with one barrier per K step.  Global loads of step k+1 are in
-// flight while step k is multiplied.
+// tile row, double buffered, with one barrier per K step; the global loads of
+// step k+1 are in flight while step k is multiplied.
 //
-// LDS layout: each operand tile is [256 rows][128 bytes], row r holding the K
-// slice of tile row r.  The 16-byte chunk c of row r sits at chunk position
-// c ^ swz(r), swz(r) = (r ^ (r >> 3)) & 7, so that 8 consecutive rows read at
-// one chunk index (the MFMA fragment read) and rows {8i + j} written at one
-// chunk index (the transposing store) both spread over all banks.
+// LDS layout: each operand tile is [256 rows][144 bytes]: row r holds the
+// 128-byte K slice of tile row r followed by 16 bytes of padding.  With the
+// 144-byte stride, 8 (or 16) consecutive rows read at one 16-byte chunk index
+// fall in distinct banks, and every fragment address is one per-lane base
+// plus a compile-time offset.  2 stages x 2 operands x 36 KiB = 144 KiB of
+// the 160 KiB LDS.
+//
+// Global loads are raw buffer loads: one 32-bit offset per lane and load,
+// fixed for the whole K loop, against a buffer descriptor whose base moves
+// with the K step.  Lanes with nothing to load use an offset beyond the
+// descriptor's range, which the hardware answers with zeros, so there are
+// no branches around loads.
 //
 // Operands come in two storage orders:
 //   natural    : element (m, k) at base[m * ld + k]  (K contiguous)
@@ -35,14 +41,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTile = 256;                        // output tile edge
-constexpr int kThreads = 256;                     // 4 waves
-constexpr int kRowBytes = 128;                    // K bytes per LDS row per stage
-constexpr int kOperandBytes = kTile * kRowBytes;  // 32 KiB
-constexpr int kStageBytes = 2 * kOperandBytes;    // A + B
-constexpr int kLdsBytes = 2 * kStageBytes;        // two stages: 128 KiB
+constexpr int kTile = 256;                         // output tile edge
+constexpr int kThreads = 256;                      // 4 waves
+constexpr int kRowBytes = 128;                     // K bytes per LDS row per stage
+constexpr int kRowStride = 144;                    // LDS bytes per row (padded)
+constexpr int kOperandBytes = kTile * kRowStride;  // 36 KiB
+constexpr int kStageBytes = 2 * kOperandBytes;     // A + B
+constexpr int kLdsBytes = 2 * kStageBytes;         // two stages: 144 KiB
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr uint32_t kOob = 0x80000000u;             // offset past every descriptor range
+constexpr int kRsrcFlags = 0x00020000;             // raw 32-bit buffer, no swizzle
 
 // bf16 values are carried as uint16_t bit patterns on the host side of the
 // templates; the MFMA sees them as __bf16.
@@ -58,166 +67,214 @@ struct Operand {
   int64_t kext;      // K readable
 };
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int r, int c) { return r * kRowBytes + ((c ^ swz(r)) << 4); }
-
-// ---------------------------------------------------------------- loads ----
-template <typename T>
-__device__ __forceinline__ void load_natural(u32x4 (&r)[8], const Operand& op, int m0, int k0,
-                                             int tid) {
-  constexpr int E = Elem<T>::kPerChunk;
-  const int64_t k = k0 + (tid & 7) * E;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t m = m0 + (tid >> 3) + 32 * i;
-    if (m < op.mext && k < op.kext)
-      r[i] = *reinterpret_cast<const u32x4*>(op.base + (m * op.ld + k) * (int64_t)sizeof(T));
-    else
-      r[i] = u32x4{0u, 0u, 0u, 0u};
-  }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, 0x7fffffff, kRsrcFlags);
 }
 
-__device__ __forceinline__ void store_natural(char* s, const u32x4 (&r)[8], int tid) {
-  const int c = tid & 7;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(s + lds_off((tid >> 3) + 32 * i, c)) = r[i];
-}
+// -------------------------------------------------------------- loaders ----
+// A loader owns the per-lane offsets of its 8 loads (fixed over the K loop)
+// and moves a descriptor base along K.
+template <typename T, bool TRANS> struct Loader;
 
-template <typename T>
-__device__ __forceinline__ void load_transposed(u32x4 (&r)[8], const Operand& op, int m0, int k0,
-                                                int tid);
-
-// bf16: 8x8 blocks, one per thread: 32 blocks along M x 8 along K.
-template <>
-__device__ __forceinline__ void load_transposed<uint16_t>(u32x4 (&r)[8], const Operand& op,
-                                                          int m0, int k0, int tid) {
-  const int64_t m = m0 + (tid & 31) * 8;
-  const int64_t kb = k0 + (tid >> 5) * 8;
+// natural: thread t loads chunk (t & 7) of tile rows (t >> 3) + 32 i.
+template <typename T> struct Loader<T, false> {
+  static constexpr int E = Elem<T>::kPerChunk;
+  uint32_t off[8];
+  int c;
+  const char* base;   // element (m0, 0)
+  int64_t kext;
+  __device__ __forceinline__ void init(const Operand& op, int m0, int tid) {
+    c = tid & 7;
+    base = op.base + (int64_t)m0 * op.ld * (int64_t)sizeof(T);
+    kext = op.kext;
+    const int r0 = tid >> 3;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t k = kb + i;
-    if (k < op.kext && m < op.mext)
-      r[i] = *reinterpret_cast<const u32x4*>(op.base + (k * op.ld + m) * 2);
-    else
-      r[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-// fp32: 4x4 blocks, two per thread: 64 blocks along M x 8 along K.
-template <>
-__device__ __forceinline__ void load_transposed<float>(u32x4 (&r)[8], const Operand& op, int m0,
-                                                       int k0, int tid) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int blk = tid + 256 * h;
-    const int64_t m = m0 + (blk & 63) * 4;
-    const int64_t kb = k0 + (blk >> 6) * 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t k = kb + i;
-      if (k < op.kext && m < op.mext)
-        r[h * 4 + i] = *reinterpret_cast<const u32x4*>(op.base + (k * op.ld + m) * 4);
-      else
-        r[h * 4 + i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 8; ++i) {
+      const int64_t m = (int64_t)m0 + r0 + 32 * i;
+      off[i] = m < op.mext ? (uint32_t)(((int64_t)(r0 + 32 * i) * op.ld + c * E) * (int64_t)sizeof(T))
+                           : kOob;
     }
   }
-}
-
-template <typename T>
-__device__ __forceinline__ void store_transposed(char* s, const u32x4 (&r)[8], int tid);
-
-template <>
-__device__ __forceinline__ void store_transposed<uint16_t>(char* s, const u32x4 (&r)[8], int tid) {
-  const int mb = tid & 31, kb = tid >> 5;
+  __device__ __forceinline__ void load(u32x4 (&r)[8], int k0) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)k0 * sizeof(T));
+    const bool kin = k0 + c * E < kext;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    u32x4 o;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t x = r[2 * w][j >> 1], y = r[2 * w + 1][j >> 1];
-      o[w] = (j & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-    }
-    *reinterpret_cast<u32x4*>(s + lds_off(mb * 8 + j, kb)) = o;
+    for (int i = 0; i < 8; ++i)
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, kin ? off[i] : kOob, 0, 0));
   }
-}
+  // LDS: row (t >> 3) + 32 i, chunk t & 7
+  __device__ __forceinline__ static int store_base(int tid) {
+    return (tid >> 3) * kRowStride + (tid & 7) * 16;
+  }
+  __device__ __forceinline__ static void store(char* s, const u32x4 (&r)[8], int tid) {
+    char* p = s + store_base(tid);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(p + i * 32 * kRowStride) = r[i];
+  }
+};
 
-template <>
-__device__ __forceinline__ void store_transposed<float>(char* s, const u32x4 (&r)[8], int tid) {
+// transposed bf16: thread t owns the 8x8 block (k block t & 7, m block t >> 3):
+// 8 loads of 16 bytes (8 m values of one k row); lanes 0..7 cover 8 k rows of
+// one 64-column span, so each load instruction reads whole 128-byte rows.
+template <> struct Loader<uint16_t, true> {
+  uint32_t off[8];
+  int kb;
+  bool min;
+  const char* base;   // element (0, m0) of the stored [k][m] matrix
+  int64_t ld, kext;
+  __device__ __forceinline__ void init(const Operand& op, int m0, int tid) {
+    kb = tid & 7;
+    const int mb = tid >> 3;
+    base = op.base + (int64_t)m0 * 2;
+    ld = op.ld;
+    kext = op.kext;
+    min = (int64_t)m0 + mb * 8 < op.mext;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int blk = tid + 256 * h;
-    const int mb = blk & 63, kb = blk >> 6;
+    for (int i = 0; i < 8; ++i) off[i] = (uint32_t)(((int64_t)(kb * 8 + i) * op.ld + mb * 8) * 2);
+  }
+  __device__ __forceinline__ void load(u32x4 (&r)[8], int k0) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)k0 * ld * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 o{r[h * 4 + 0][j], r[h * 4 + 1][j], r[h * 4 + 2][j], r[h * 4 + 3][j]};
-      *reinterpret_cast<u32x4*>(s + lds_off(mb * 4 + j, kb)) = o;
+    for (int i = 0; i < 8; ++i) {
+      const bool ok = min && (k0 + kb * 8 + i < kext);
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off[i] : kOob, 0, 0));
     }
   }
-}
+  // LDS: rows (t >> 3) * 8 + j, chunk t & 7; 8x8 transpose in registers.
+  __device__ __forceinline__ static void store(char* s, const u32x4 (&r)[8], int tid) {
+    char* p = s + (tid >> 3) * 8 * kRowStride + (tid & 7) * 16;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = r[2 * w][j >> 1], y = r[2 * w + 1][j >> 1];
+        o[w] = (j & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+      }
+      *reinterpret_cast<u32x4*>(p + j * kRowStride) = o;
+    }
+  }
+};
 
-template <typename T, bool TRANS>
-__device__ __forceinline__ void load_op(u32x4 (&r)[8], const Operand& op, int m0, int k0, int tid) {
-  if constexpr (TRANS) load_transposed<T>(r, op, m0, k0, tid);
-  else load_natural<T>(r, op, m0, k0, tid);
-}
-
-template <typename T, bool TRANS>
-__device__ __forceinline__ void store_op(char* s, const u32x4 (&r)[8], int tid) {
-  if constexpr (TRANS) store_transposed<T>(s, r, tid);
-  else store_natural(s, r, tid);
-}
+// transposed fp32: 4x4 blocks, two per thread: block b = t + 256 h has
+// k block b & 7 and m block b >> 3 (64 m blocks of 4).
+template <> struct Loader<float, true> {
+  uint32_t off[8];
+  int kb;
+  bool min[2];
+  const char* base;
+  int64_t ld, kext;
+  __device__ __forceinline__ void init(const Operand& op, int m0, int tid) {
+    kb = tid & 7;
+    base = op.base + (int64_t)m0 * 4;
+    ld = op.ld;
+    kext = op.kext;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int mb = (tid + 256 * h) >> 3;
+      min[h] = (int64_t)m0 + mb * 4 < op.mext;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        off[h * 4 + i] = (uint32_t)(((int64_t)(kb * 4 + i) * op.ld + mb * 4) * 4);
+    }
+  }
+  __device__ __forceinline__ void load(u32x4 (&r)[8], int k0) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)k0 * ld * 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = min[h] && (k0 + kb * 4 + i < kext);
+        r[h * 4 + i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off[h * 4 + i] : kOob, 0, 0));
+      }
+  }
+  __device__ __forceinline__ static void store(char* s, const u32x4 (&r)[8], int tid) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int mb = (tid + 256 * h) >> 3;
+      char* p = s + mb * 4 * kRowStride + (tid & 7) * 16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 o{r[h * 4 + 0][j], r[h * 4 + 1][j], r[h * 4 + 2][j], r[h * 4 + 3][j]};
+        *reinterpret_cast<u32x4*>(p + j * kRowStride) = o;
+      }
+    }
+  }
+};
 
 // ------------------------------------------------------------ multiply ----
 // Lane l of a wave reads, for tile row (wave base + 32 i + l % 32), chunk
 // (2 ks + l / 32): 8 consecutive K values for bf16, 4 for fp32.  A and B use
 // the same lane -> K mapping, so every MFMA pairs equal K indices.
+__device__ __forceinline__ int frag_base(int wrow, int lane) {
+  return (wrow + (lane & 31)) * kRowStride + (lane >> 5) * 16;
+}
+
+// fresh: the first MFMA of every accumulator takes C = 0 (start of a tile).
 template <typename T>
 __device__ __forceinline__ void mma_stage(const char* sA, const char* sB, f32x16 (&acc)[4][4],
-                                          int wm, int wn, int lane);
+                                          bool fresh);
 
 template <>
 __device__ __forceinline__ void mma_stage<uint16_t>(const char* sA, const char* sB,
-                                                    f32x16 (&acc)[4][4], int wm, int wn,
-                                                    int lane) {
-  const int lr = lane & 31, hf = lane >> 5;
+                                                    f32x16 (&acc)[4][4], bool fresh) {
+  const f32x16 zero = {};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     bf16x8 a[4], b[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wm * 128 + i * 32 + lr, ks * 2 + hf));
+      a[i] = *reinterpret_cast<const bf16x8*>(sA + i * 32 * kRowStride + ks * 32);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(sB + lds_off(wn * 128 + j * 32 + lr, ks * 2 + hf));
+      b[j] = *reinterpret_cast<const bf16x8*>(sB + j * 32 * kRowStride + ks * 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j],
+                                                            (ks == 0 && fresh) ? zero : acc[i][j],
+                                                            0, 0, 0);
   }
 }
 
 template <>
 __device__ __forceinline__ void mma_stage<float>(const char* sA, const char* sB,
-                                                 f32x16 (&acc)[4][4], int wm, int wn, int lane) {
-  const int lr = lane & 31, hf = lane >> 5;
+                                                 f32x16 (&acc)[4][4], bool fresh) {
+  const f32x16 zero = {};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     f32x4 a[4], b[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const f32x4*>(sA + lds_off(wm * 128 + i * 32 + lr, ks * 2 + hf));
+      a[i] = *reinterpret_cast<const f32x4*>(sA + i * 32 * kRowStride + ks * 32);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const f32x4*>(sB + lds_off(wn * 128 + j * 32 + lr, ks * 2 + hf));
+      b[j] = *reinterpret_cast<const f32x4*>(sB + j * 32 * kRowStride + ks * 32);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][t], b[j][t], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+              a[i][t], b[j][t], (ks == 0 && t == 0 && fresh) ? zero : acc[i][j], 0, 0, 0);
   }
+}
+
+// Pins the accumulators to AGPRs at a tile's end and waits out the MFMA
+// result latency before VALU code reads them (an 8-pass 32x32 MFMA needs 11
+// wait states before a VALU read of its result; this gives 34).  Passing every
+// block as an "+a" operand orders the fence after all MFMAs of the tile and
+// before every read, and keeps the register allocator from moving the
+// accumulators into VGPRs around an epilogue.
+__device__ __forceinline__ void acc_fence(f32x16 (&acc)[4][4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 1"
+               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                 "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]),
+                 "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
+                 "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
 }
 
 struct AllActive {
@@ -245,31 +302,39 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
   int kb = 0;
   while (kb < nk && !active(kb)) ++kb;
   if (kb >= nk) return;
+  Loader<T, AT> la;
+  Loader<T, BT> lb;
+  la.init(A, m0, tid);
+  lb.init(B, n0, tid);
+  const int fa = frag_base(wm * 128, lane), fb = frag_base(wn * 128, lane);
   u32x4 ra[8], rb[8];
-  load_op<T, AT>(ra, A, m0, kb * KS, tid);
-  load_op<T, BT>(rb, B, n0, kb * KS, tid);
-  store_op<T, AT>(lds, ra, tid);
-  store_op<T, BT>(lds + kOperandBytes, rb, tid);
+  la.load(ra, kb * KS);
+  lb.load(rb, kb * KS);
+  Loader<T, AT>::store(lds, ra, tid);
+  Loader<T, BT>::store(lds + kOperandBytes, rb, tid);
   __syncthreads();
   int buf = 0;
-  for (;;) {
+  // single-exit loop: the accumulators have one loop-carried definition
+  while (kb < nk) {
     int nxt = kb + 1;
     while (nxt < nk && !active(nxt)) ++nxt;
     const bool more = nxt < nk;
     if (more) {
-      load_op<T, AT>(ra, A, m0, nxt * KS, tid);
-      load_op<T, BT>(rb, B, n0, nxt * KS, tid);
+      la.load(ra, nxt * KS);
+      lb.load(rb, nxt * KS);
     }
     const char* s = lds + buf * kStageBytes;
-    mma_stage<T>(s, s + kOperandBytes, acc, wm, wn, lane);
-    if (!more) break;
+    mma_stage<T>(s + fa, s + kOperandBytes + fb, acc, false);
+    if (more) {
+      char* w = lds + (buf ^ 1) * kStageBytes;
+      Loader<T, AT>::store(w, ra, tid);
+      Loader<T, BT>::store(w + kOperandBytes, rb, tid);
+      __syncthreads();
+    }
     buf ^= 1;
-    char* w = lds + buf * kStageBytes;
-    store_op<T, AT>(w, ra, tid);
-    store_op<T, BT>(w + kOperandBytes, rb, tid);
-    __syncthreads();
     kb = nxt;
   }
+  acc_fence(acc);
   __syncthreads();  // LDS may be reused by the caller
 }
 

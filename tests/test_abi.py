@@ -122,7 +122,7 @@ def test_workspace_within_64_mib(name, N, D, V, dt):
                                                    else torch.float32)
     assert p["band_rows"] % 256 == 0 and p["band_vocab"] % 256 == 0
     assert p["n_bands_rows"] * p["band_rows"] >= N and p["n_bands_vocab"] * p["band_vocab"] >= V
-    assert p["fwd_vocab_splits"] * 256 <= ((V + 255) // 256) * 256
+    assert p["fwd_band_rows"] % 256 == 0 and p["fwd_band_rows"] >= 256
 
 
 def test_budget_shrinks_bands_and_reports_overflow():

@@ -224,10 +224,16 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
             w.flags, w.flagsT);
       }));
       FLCE_TRY(launch(FLCE_K_BWD_GRAD, prof, s, [&] {
-        flce::bwd_grad_kernel<T><<<dim3(TNn * Td + TMv * Td), dim3(flce::kThreads), 0, s>>>(
-            static_cast<const T*>(H), static_cast<const T*>(W), static_cast<const T*>(w.dz),
-            w.flags, w.flagsT, dH, dW, N, D, V, band, TNn, TMv, Td, bv > 0 ? 1 : 0,
-            bn > 0 ? 1 : 0);
+        const dim3 grid(TNn * Td + TMv * Td), block(flce::kThreads);
+        const int bh = bv > 0 ? 1 : 0, bw = bn > 0 ? 1 : 0;
+        if (d->filter_eps > 0.f)
+          flce::bwd_grad_kernel<T, true><<<grid, block, 0, s>>>(
+              static_cast<const T*>(H), static_cast<const T*>(W), static_cast<const T*>(w.dz),
+              w.flags, w.flagsT, dH, dW, N, D, V, band, TNn, TMv, Td, bh, bw);
+        else
+          flce::bwd_grad_kernel<T, false><<<grid, block, 0, s>>>(
+              static_cast<const T*>(H), static_cast<const T*>(W), static_cast<const T*>(w.dz),
+              w.flags, w.flagsT, dH, dW, N, D, V, band, TNn, TMv, Td, bh, bw);
       }));
     }
   }

@@ -21,6 +21,7 @@
 //                       half, done as two ordinary MFMA GEMMs without locks).
 #pragma once
 
+#include "tile_dma.hpp"
 #include "tile_mma.hpp"
 
 namespace flce {
@@ -31,6 +32,20 @@ struct Header {           // first 256 bytes of the workspace
   float gscale;           // g for mean / sum: dloss / max(count, 1) or dloss
   float pad[61];
 };
+
+// K step (elements) of one pass of a tile contraction, for both element types.
+constexpr int kStepK = 32;
+
+// A 256x256 tile contraction over K = [0, K): bf16 through the LDS-DMA core,
+// fp32 through the register-staged core.  active(s) covers K [32 s, 32 s + 32).
+template <typename T, bool AT, bool BT, class Active>
+__device__ __forceinline__ void tile_contract(const Operand& A, const Operand& B, int m0, int n0,
+                                              int K, const Active& active, f32x16 (&acc)[4][4],
+                                              char* lds) {
+  const int nsteps = (K + kStepK - 1) / kStepK;
+  if constexpr (sizeof(T) == 2) gemm_tile_dma<AT, BT>(A, B, m0, n0, nsteps, active, acc, lds);
+  else gemm_tile<T, AT, BT>(A, B, m0, n0, nsteps, active, acc, lds);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -115,9 +130,8 @@ fwd_lse_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* 
   const int wm = wave >> 1, wn = wave & 1;
   const Operand A{reinterpret_cast<const char*>(W), D, V, D};
   const Operand B{reinterpret_cast<const char*>(H), D, N, D};
-  const int nk = (D + kKStep<T> - 1) / kKStep<T>;
   f32x16 acc[4][4];
-  gemm_tile<T, false, false>(A, B, v0, n0, nk, AllActive{}, acc, lds);
+  tile_contract<T, false, false>(A, B, v0, n0, D, AllActive{}, acc, lds);
 
   const int vw = v0 + wm * 128;  // first vocabulary row of this wave's block
   int rel[4];
@@ -328,9 +342,8 @@ bwd_dz_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* _
 
   const Operand A{reinterpret_cast<const char*>(W), D, V, D};
   const Operand B{reinterpret_cast<const char*>(H), D, N, D};
-  const int nk = (D + kKStep<T> - 1) / kKStep<T>;
   f32x16 acc[4][4];
-  gemm_tile<T, false, false>(A, B, v0, n0, nk, AllActive{}, acc, lds);
+  tile_contract<T, false, false>(A, B, v0, n0, D, AllActive{}, acc, lds);
 
   float g[4], ml[4];
   int rel[4];
@@ -433,17 +446,38 @@ bwd_dz_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* _
   }
 }
 
-struct SkipRowsOfFlags {   // active unless all four flags of this K step are set
-  const uint8_t* base;     // first of the four flags of K step 0
-  int step_stride;         // bytes between consecutive 64-wide K blocks
-  int kshift;              // log2(64 / K elements per stage)
-  __device__ __forceinline__ bool operator()(int kb) const {
-    const uint32_t f = *reinterpret_cast<const uint32_t*>(base + (kb >> kshift) * step_stride);
-    return f != 0x01010101u;
+// Active K steps of a contraction whose K runs over 64-wide filter blocks: a
+// step is skipped when all four flags of its 64-block (one per 64 output
+// rows of the tile) are set.  The flags are read once, before the K loop,
+// into a 64-bit mask: scalar loads inside the loop would share the LDS wait
+// counter with the fragment reads and stall them.
+struct SkipRowsOfFlags {
+  const uint8_t* base;     // first of the four flags of 64-block 0
+  int step_stride;         // bytes between consecutive 64-blocks
+  uint64_t mask = 0;       // bit b: 64-block b is active
+  __device__ __forceinline__ void prepare(int nsteps) {
+    const int nb = (nsteps + 1) >> 1;   // K steps of 32 -> 64-blocks (<= 64)
+    uint64_t m = 0;
+    for (int b = 0; b < nb; ++b) {
+      const uint32_t f = *reinterpret_cast<const uint32_t*>(base + b * step_stride);
+      m |= (uint64_t)(f != 0x01010101u) << b;
+    }
+    mask = m;
+  }
+  __device__ __forceinline__ bool operator()(int s) const { return (mask >> (s >> 1)) & 1; }
+  // first active step >= s (nsteps if none)
+  __device__ __forceinline__ int next(int s, int nsteps) const {
+    const int b = s >> 1;
+    if (b >= 64) return nsteps;
+    const uint64_t rest = mask >> b;
+    if (rest == 0) return nsteps;
+    const int nb = b + __builtin_ctzll(rest);
+    const int ns = nb == b ? s : 2 * nb;
+    return ns < nsteps ? ns : nsteps;
   }
 };
 
-template <typename T>
+template <typename T, bool FILTER>
 __global__ void __launch_bounds__(kThreads, 1)
 bwd_grad_kernel(const T* __restrict__ H, const T* __restrict__ W, const T* __restrict__ dz,
                 const uint8_t* __restrict__ flags, const uint8_t* __restrict__ flagsT,
@@ -453,8 +487,6 @@ bwd_grad_kernel(const T* __restrict__ H, const T* __restrict__ W, const T* __res
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  constexpr int KS = kKStep<T>;
-  constexpr int kshift = (KS == 64) ? 0 : 1;
   f32x16 acc[4][4];
   float* out;
   int mvalid, beta, tm, tn;
@@ -465,9 +497,12 @@ bwd_grad_kernel(const T* __restrict__ H, const T* __restrict__ W, const T* __res
     const int kpad = (band.vs_cur + kTile - 1) / kTile * kTile;
     const Operand A{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T3m * kTile, kpad};
     const Operand B{reinterpret_cast<const char*>(W + (int64_t)band.vb0 * D), D, D, band.vs_cur};
-    const SkipRowsOfFlags act{flagsT + tm * 4, band.frows, kshift};
-    gemm_tile<T, false, true>(A, B, tm * kTile, tn * kTile, (band.vs_cur + KS - 1) / KS, act, acc,
-                              lds);
+    if constexpr (FILTER) {
+      const SkipRowsOfFlags act{flagsT + tm * 4, band.frows};
+      tile_contract<T, false, true>(A, B, tm * kTile, tn * kTile, band.vs_cur, act, acc, lds);
+    } else {
+      tile_contract<T, false, true>(A, B, tm * kTile, tn * kTile, band.vs_cur, AllActive{}, acc, lds);
+    }
     out = dH + (int64_t)band.nb0 * D;
     mvalid = band.ns_cur;
     beta = beta_h;
@@ -477,9 +512,12 @@ bwd_grad_kernel(const T* __restrict__ H, const T* __restrict__ W, const T* __res
     const Operand A{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2m * kTile,
                     band.ns_cur};
     const Operand B{reinterpret_cast<const char*>(H + (int64_t)band.nb0 * D), D, D, band.ns_cur};
-    const SkipRowsOfFlags act{flags + tm * 4, band.fcols, kshift};
-    gemm_tile<T, true, true>(A, B, tm * kTile, tn * kTile, (band.ns_cur + KS - 1) / KS, act, acc,
-                             lds);
+    if constexpr (FILTER) {
+      const SkipRowsOfFlags act{flags + tm * 4, band.fcols};
+      tile_contract<T, true, true>(A, B, tm * kTile, tn * kTile, band.ns_cur, act, acc, lds);
+    } else {
+      tile_contract<T, true, true>(A, B, tm * kTile, tn * kTile, band.ns_cur, AllActive{}, acc, lds);
+    }
     out = dW + (int64_t)band.vb0 * D;
     mvalid = band.vs_cur;
     beta = beta_w;

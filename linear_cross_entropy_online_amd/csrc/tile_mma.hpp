@@ -278,7 +278,9 @@ __device__ __forceinline__ void acc_fence(f32x16 (&acc)[4][4]) {
 }
 
 struct AllActive {
+  __device__ __forceinline__ void prepare(int) {}
   __device__ __forceinline__ bool operator()(int) const { return true; }
+  __device__ __forceinline__ int next(int s, int nsteps) const { return s < nsteps ? s : nsteps; }
 };
 
 // acc[i][j] (wave (wm, wn)) receives C[m0 + 128 wm + 32 i + row][n0 + 128 wn + 32 j + col]
@@ -287,8 +289,9 @@ struct AllActive {
 // `active(kb)` must give the same answer in every thread of the workgroup.
 template <typename T, bool AT, bool BT, class Active>
 __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, int m0, int n0,
-                                          int nk, const Active& active, f32x16 (&acc)[4][4],
+                                          int nk, Active active, f32x16 (&acc)[4][4],
                                           char* lds) {
+  active.prepare(nk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   constexpr int KS = kKStep<T>;
@@ -299,8 +302,7 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  int kb = 0;
-  while (kb < nk && !active(kb)) ++kb;
+  int kb = active.next(0, nk);
   if (kb >= nk) return;
   Loader<T, AT> la;
   Loader<T, BT> lb;
@@ -316,8 +318,7 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
   int buf = 0;
   // single-exit loop: the accumulators have one loop-carried definition
   while (kb < nk) {
-    int nxt = kb + 1;
-    while (nxt < nk && !active(nxt)) ++nxt;
+    const int nxt = active.next(kb + 1, nk);
     const bool more = nxt < nk;
     if (more) {
       la.load(ra, nxt * KS);

@@ -9,7 +9,7 @@
 //   for each band of NS token rows:
 //     for each band of VS vocabulary rows:
 //       bwd_dz_kernel    grid = ceil(VS/256) x ceil(NS/256)
-//       bwd_grad_kernel  grid = ceil(NS/256) x ceil(D/256) + ceil(VS/256) x ceil(D/256)
+//       bwd_grad_kernel  grid = ceil(D/256) x ceil(NS/256) + ceil(D/256) x ceil(VS/256)
 // dH of a token band accumulates over the vocabulary bands and dW of a
 // vocabulary band over the token bands; the first contribution stores, the
 // rest add, all in stream order, so the result is deterministic.
@@ -41,7 +41,7 @@ struct Plan {
   int NS, VS;          // backward band sizes (multiples of 256)
   int nbn, nbv;        // backward band counts
   int frows, fcols;    // flag grid of a backward band
-  int nblk;            // combine blocks
+  int nblk;            // combine blocks (16 rows each)
   size_t big;          // bytes shared by the forward partials and the dZ band
   size_t off_zy, off_bsum, off_bcnt, off_flags, off_flagsT, off_big, total;
 };
@@ -92,7 +92,7 @@ int make_plan(const flce_desc* d, Plan& p) {
   p.es = d->in_dtype == FLCE_BF16 ? 2 : 4;
   p.Tv = int(cdiv(p.V, flce::kTile));
   const int64_t Npad = cdiv(std::max<int64_t>(p.N, 1), 256) * 256;
-  p.nblk = int(Npad / 256);
+  p.nblk = int(cdiv(std::max<int64_t>(p.N, 1), flce::kCombineRows));   // one per combine block
   p.NS = int(std::min<int64_t>(kMaxBand, Npad));
   p.VS = int(std::min<int64_t>(kMaxBand, cdiv(p.V, 256) * 256));
   const uint64_t budget = d->ws_budget_bytes ? d->ws_budget_bytes : kDefaultBudget;
@@ -187,7 +187,7 @@ int run_forward(const flce_desc* d, const Plan& p, const void* H, const void* W,
           ns, p.Tv, TNn, pm, ps, w.zy, w.hdr);
     }));
     FLCE_TRY(launch(FLCE_K_LSE_COMBINE, prof, s, [&] {
-      flce::lse_combine_kernel<<<dim3(TNn), dim3(256), 0, s>>>(
+      flce::lse_combine_kernel<<<dim3(int(cdiv(ns, flce::kCombineRows))), dim3(256), 0, s>>>(
           pm, ps, w.zy, y, N, V, p.Tv, nb0, ns, d->ignore_index, lse, loss_rows, w.bsum, w.bcnt,
           w.hdr);
     }));

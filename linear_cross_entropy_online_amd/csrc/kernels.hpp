@@ -202,27 +202,48 @@ __device__ __forceinline__ void block_reduce_256(double& s, int& c, double* sh_s
   c = sh_c[0];
 }
 
+// One block = 16 token rows x 16 slices of the vocabulary tiles: slice sl
+// merges partials sl, sl + 16, ... of its row (online, rescaling only when the
+// max grows), then the 16 slice results of a row merge in slice order.
+constexpr int kCombineRows = 16;
+
 __global__ void __launch_bounds__(256)
 lse_combine_kernel(const float* __restrict__ part_m, const float* __restrict__ part_s,
                    const float* __restrict__ zy, const int64_t* __restrict__ y, int N, int V,
                    int Tv, int nb0, int ns, int64_t ignore, float* __restrict__ lse,
                    float* __restrict__ loss_rows, double* __restrict__ blk_sum,
                    int* __restrict__ blk_cnt, Header* __restrict__ hdr) {
+  __shared__ float sh_m[16][kCombineRows], sh_sum[16][kCombineRows];
   __shared__ double sh_s[256];
   __shared__ int sh_c[256];
-  const int nl = blockIdx.x * 256 + threadIdx.x;   // row within the band
-  const int n = nb0 + nl;
+  const int r = threadIdx.x % kCombineRows, sl = threadIdx.x / kCombineRows;
+  const int nl = blockIdx.x * kCombineRows + r;   // row within the band
+  float M = -INFINITY, S = 0.f;
+  if (nl < ns) {
+    for (int k = sl; k < Tv; k += 16) {
+      const float m = part_m[(int64_t)k * ns + nl], sk = part_s[(int64_t)k * ns + nl];
+      if (m == -INFINITY) continue;
+      if (m <= M) {
+        S += sk * fast_exp2((m - M) * kLog2e);
+      } else {
+        S = S * fast_exp2((M - m) * kLog2e) + sk;   // M = -inf: S = 0 * 0 + sk
+        M = m;
+      }
+    }
+  }
+  sh_m[sl][r] = M;
+  sh_sum[sl][r] = S;
+  __syncthreads();
   double s = 0.0;
   int c = 0;
-  if (nl < ns) {
-    float M = -INFINITY;
-    for (int k = 0; k < Tv; ++k) M = fmaxf(M, part_m[(int64_t)k * ns + nl]);
-    float S = 0.f;
-    for (int k = 0; k < Tv; ++k) {
-      const float m = part_m[(int64_t)k * ns + nl];
-      S += part_s[(int64_t)k * ns + nl] * fast_exp2((m - M) * kLog2e);
-    }
-    const float l = M + fast_log2(S) * kLn2;
+  if (sl == 0 && nl < ns) {
+    float Mx = -INFINITY;
+    for (int q = 0; q < 16; ++q) Mx = fmaxf(Mx, sh_m[q][r]);
+    float St = 0.f;
+    for (int q = 0; q < 16; ++q)
+      St += sh_sum[q][r] * fast_exp2((sh_m[q][r] - Mx) * kLog2e);
+    const float l = Mx + fast_log2(St) * kLn2;
+    const int n = nb0 + nl;
     lse[n] = l;
     const int64_t yy = y[n];
     float lr = 0.f;
@@ -240,8 +261,8 @@ lse_combine_kernel(const float* __restrict__ part_m, const float* __restrict__ p
   }
   block_reduce_256(s, c, sh_s, sh_c);
   if (threadIdx.x == 0) {
-    blk_sum[nb0 / 256 + blockIdx.x] = s;
-    blk_cnt[nb0 / 256 + blockIdx.x] = c;
+    blk_sum[nb0 / kCombineRows + blockIdx.x] = s;
+    blk_cnt[nb0 / kCombineRows + blockIdx.x] = c;
   }
 }
 
@@ -477,65 +498,74 @@ struct SkipRowsOfFlags {
   }
 };
 
+// dH[band rows] (+)= dZ W[band vocab] and dW[band vocab] (+)= dZ^T H[band rows]
+// in one launch.  Both products are computed transposed, C[d][row], so that
+// each lane's accumulator column holds 4 consecutive d values of one output
+// row: the fp32 read-modify-write is one 16-byte access per 4 values.
+//   dH^T tile: A = W_band^T (stored [v][d]), B = dZ (stored [n][v]), K = v
+//   dW^T tile: A = H_band^T (stored [n][d]), B = dZ^T (stored [n][v]), K = n
 template <typename T, bool FILTER>
 __global__ void __launch_bounds__(kThreads, 1)
 bwd_grad_kernel(const T* __restrict__ H, const T* __restrict__ W, const T* __restrict__ dz,
                 const uint8_t* __restrict__ flags, const uint8_t* __restrict__ flagsT,
                 float* __restrict__ dH, float* __restrict__ dW, int N, int D, int V,
-                BandArgs band, int T3m, int T2m, int Td, int beta_h, int beta_w) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+                BandArgs band, int T3n, int T2n, int Td, int beta_h, int beta_w) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   f32x16 acc[4][4];
   float* out;
-  int mvalid, beta, tm, tn;
-  const int T3 = T3m * Td;
+  int rvalid, beta, td, tr;
+  const int T3 = Td * T3n;
   if (t < T3) {
-    // dH[band rows, :] (+)= dZ[band rows, band vocab] . W[band vocab, :]
-    grouped_tile(t, T3m, Td, 4, tm, tn);
+    grouped_tile(t, Td, T3n, 4, td, tr);   // d tile, band row tile
+    const Operand A{reinterpret_cast<const char*>(W + (int64_t)band.vb0 * D), D, D, band.vs_cur};
     const int kpad = (band.vs_cur + kTile - 1) / kTile * kTile;
-    const Operand A{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T3m * kTile, kpad};
-    const Operand B{reinterpret_cast<const char*>(W + (int64_t)band.vb0 * D), D, D, band.vs_cur};
+    const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T3n * kTile, kpad};
     if constexpr (FILTER) {
-      const SkipRowsOfFlags act{flagsT + tm * 4, band.frows};
-      tile_contract<T, false, true>(A, B, tm * kTile, tn * kTile, band.vs_cur, act, acc, lds);
+      const SkipRowsOfFlags act{flagsT + tr * 4, band.frows};
+      tile_contract<T, true, false>(A, B, td * kTile, tr * kTile, band.vs_cur, act, acc, lds);
     } else {
-      tile_contract<T, false, true>(A, B, tm * kTile, tn * kTile, band.vs_cur, AllActive{}, acc, lds);
+      tile_contract<T, true, false>(A, B, td * kTile, tr * kTile, band.vs_cur, AllActive{}, acc, lds);
     }
     out = dH + (int64_t)band.nb0 * D;
-    mvalid = band.ns_cur;
+    rvalid = band.ns_cur;
     beta = beta_h;
   } else {
-    // dW[band vocab, :] (+)= dZ[band rows, band vocab]^T . H[band rows, :]
-    grouped_tile(t - T3, T2m, Td, 4, tm, tn);
-    const Operand A{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2m * kTile,
-                    band.ns_cur};
-    const Operand B{reinterpret_cast<const char*>(H + (int64_t)band.nb0 * D), D, D, band.ns_cur};
+    grouped_tile(t - T3, Td, T2n, 4, td, tr);   // d tile, band vocabulary tile
+    const Operand A{reinterpret_cast<const char*>(H + (int64_t)band.nb0 * D), D, D, band.ns_cur};
+    const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2n * kTile, band.ns_cur};
     if constexpr (FILTER) {
-      const SkipRowsOfFlags act{flags + tm * 4, band.fcols};
-      tile_contract<T, true, true>(A, B, tm * kTile, tn * kTile, band.ns_cur, act, acc, lds);
+      const SkipRowsOfFlags act{flags + tr * 4, band.fcols};
+      tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, act, acc, lds);
     } else {
-      tile_contract<T, true, true>(A, B, tm * kTile, tn * kTile, band.ns_cur, AllActive{}, acc, lds);
+      tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, AllActive{}, acc, lds);
     }
     out = dW + (int64_t)band.vb0 * D;
-    mvalid = band.vs_cur;
+    rvalid = band.vs_cur;
     beta = beta_w;
   }
-  const int mw = tm * kTile + wm * 128, dw0 = tn * kTile + wn * 128;
+  // acc[i][j][4q + e]: d = dw + 32 i + 8 q + 4 (lane / 32) + e, row = rw + 32 j + lane % 32
+  const int dw = td * kTile + wm * 128 + 4 * (lane >> 5), rw = tr * kTile + wn * 128 + (lane & 31);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int row = rw + 32 * j;
+    if (row >= rvalid) continue;
+    float* orow = out + (int64_t)row * D;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = mw + acc_row(i, r, lane);
-      if (m >= mvalid) continue;
-      float* row = out + (int64_t)m * D;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = dw0 + j * 32 + (lane & 31);
-        if (d < D) row[d] = beta ? row[d] + acc[i][j][r] : acc[i][j][r];
+      for (int q = 0; q < 4; ++q) {
+        const int d = dw + 32 * i + 8 * q;
+        if (d >= D) continue;
+        f32x4 v{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        f32x4* p = reinterpret_cast<f32x4*>(orow + d);
+        if (beta) v += *p;
+        *p = v;
       }
-    }
+  }
+  (void)N;
   (void)V;
 }
 

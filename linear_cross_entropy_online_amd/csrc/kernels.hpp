@@ -33,17 +33,27 @@ struct Header {           // first 256 bytes of the workspace
   float pad[61];
 };
 
-// K step (elements) of one pass of a tile contraction, for both element types.
-constexpr int kStepK = 32;
+// K elements of one pass of a tile contraction: 64 for bf16 (LDS-DMA core,
+// whole 128-byte lines per operand row), 32 for fp32 (register-staged core).
+template <typename T>
+constexpr int step_k() { return sizeof(T) == 2 ? kDmaKStep : 32; }
 
 // A 256x256 tile contraction over K = [0, K): bf16 through the LDS-DMA core,
-// fp32 through the register-staged core.  active(s) covers K [32 s, 32 s + 32).
+// fp32 through the register-staged core.  active(s) covers K
+// [s step_k, (s + 1) step_k).
 template <typename T, bool AT, bool BT, class Active>
 __device__ __forceinline__ void tile_contract(const Operand& A, const Operand& B, int m0, int n0,
                                               int K, const Active& active, f32x16 (&acc)[4][4],
                                               char* lds) {
-  const int nsteps = (K + kStepK - 1) / kStepK;
-  if constexpr (sizeof(T) == 2) gemm_tile_dma<AT, BT>(A, B, m0, n0, nsteps, active, acc, lds);
+  const int nsteps = (K + step_k<T>() - 1) / step_k<T>();
+  // Every contraction here visits its tiles in the grouped order of
+  // grouped_tile with 4 tile rows (A side) per group, so the ~32 workgroups
+  // that run together on one XCD form about 4 A blocks x 8 B blocks: an A
+  // block is shared by 8 consecutive B tiles, a B block by 4 consecutive A
+  // tiles, and consecutive tiles have distinct residues.
+  if constexpr (sizeof(T) == 2)
+    gemm_tile_dma<AT, BT>(A, B, m0, n0, nsteps, active, acc, lds,
+                          L2Split{(n0 / kTile) & 7, 8}, L2Split{(m0 / kTile) & 3, 4});
   else gemm_tile<T, AT, BT>(A, B, m0, n0, nsteps, active, acc, lds);
 }
 
@@ -471,13 +481,17 @@ bwd_dz_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* _
 // step is skipped when all four flags of its 64-block (one per 64 output
 // rows of the tile) are set.  The flags are read once, before the K loop,
 // into a 64-bit mask: scalar loads inside the loop would share the LDS wait
-// counter with the fragment reads and stall them.
+// counter with the fragment reads and stall them.  STEP is the K width of a
+// step (64 or 32).
+template <int STEP>
 struct SkipRowsOfFlags {
+  static_assert(STEP == 64 || STEP == 32, "step width");
+  static constexpr int kShift = STEP == 64 ? 0 : 1;   // log2(steps per 64-block)
   const uint8_t* base;     // first of the four flags of 64-block 0
   int step_stride;         // bytes between consecutive 64-blocks
   uint64_t mask = 0;       // bit b: 64-block b is active
   __device__ __forceinline__ void prepare(int nsteps) {
-    const int nb = (nsteps + 1) >> 1;   // K steps of 32 -> 64-blocks (<= 64)
+    const int nb = (nsteps + (1 << kShift) - 1) >> kShift;   // 64-blocks (<= 64)
     uint64_t m = 0;
     for (int b = 0; b < nb; ++b) {
       const uint32_t f = *reinterpret_cast<const uint32_t*>(base + b * step_stride);
@@ -485,15 +499,15 @@ struct SkipRowsOfFlags {
     }
     mask = m;
   }
-  __device__ __forceinline__ bool operator()(int s) const { return (mask >> (s >> 1)) & 1; }
+  __device__ __forceinline__ bool operator()(int s) const { return (mask >> (s >> kShift)) & 1; }
   // first active step >= s (nsteps if none)
   __device__ __forceinline__ int next(int s, int nsteps) const {
-    const int b = s >> 1;
+    const int b = s >> kShift;
     if (b >= 64) return nsteps;
     const uint64_t rest = mask >> b;
     if (rest == 0) return nsteps;
     const int nb = b + __builtin_ctzll(rest);
-    const int ns = nb == b ? s : 2 * nb;
+    const int ns = nb == b ? s : (nb << kShift);
     return ns < nsteps ? ns : nsteps;
   }
 };
@@ -524,7 +538,7 @@ bwd_grad_kernel(const T* __restrict__ H, const T* __restrict__ W, const T* __res
     const int kpad = (band.vs_cur + kTile - 1) / kTile * kTile;
     const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T3n * kTile, kpad};
     if constexpr (FILTER) {
-      const SkipRowsOfFlags act{flagsT + tr * 4, band.frows};
+      const SkipRowsOfFlags<step_k<T>()> act{flagsT + tr * 4, band.frows};
       tile_contract<T, true, false>(A, B, td * kTile, tr * kTile, band.vs_cur, act, acc, lds);
     } else {
       tile_contract<T, true, false>(A, B, td * kTile, tr * kTile, band.vs_cur, AllActive{}, acc, lds);
@@ -537,7 +551,7 @@ bwd_grad_kernel(const T* __restrict__ H, const T* __restrict__ W, const T* __res
     const Operand A{reinterpret_cast<const char*>(H + (int64_t)band.nb0 * D), D, D, band.ns_cur};
     const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2n * kTile, band.ns_cur};
     if constexpr (FILTER) {
-      const SkipRowsOfFlags act{flags + tr * 4, band.fcols};
+      const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols};
       tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, act, acc, lds);
     } else {
       tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, AllActive{}, acc, lds);
@@ -546,23 +560,43 @@ bwd_grad_kernel(const T* __restrict__ H, const T* __restrict__ W, const T* __res
     rvalid = band.vs_cur;
     beta = beta_w;
   }
-  // acc[i][j][4q + e]: d = dw + 32 i + 8 q + 4 (lane / 32) + e, row = rw + 32 j + lane % 32
-  const int dw = td * kTile + wm * 128 + 4 * (lane >> 5), rw = tr * kTile + wn * 128 + (lane & 31);
+  // acc[i][j][4q + e]: d = dw + 32 i + 8 q + 4 (lane / 32) + e, row = rw + 32 j + lane % 32.
+  // Buffer accesses relative to the tile's first output row: an offset past
+  // the output (row >= rvalid or d >= D) reads zeros and drops the store, so
+  // the 16 loads of a row group go out together, with no branches between
+  // them.
+  const int row0 = tr * kTile;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(reinterpret_cast<const char*>(out + (int64_t)row0 * D));
+  const int dw = td * kTile + wm * 128 + 4 * (lane >> 5);
+  const int lw = wn * 128 + (lane & 31);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int row = rw + 32 * j;
-    if (row >= rvalid) continue;
-    float* orow = out + (int64_t)row * D;
+    const int lr = lw + 32 * j;
+    const bool rok = row0 + lr < rvalid;
+    uint32_t off[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int d = dw + 32 * i + 8 * q;
-        if (d >= D) continue;
-        f32x4 v{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        f32x4* p = reinterpret_cast<f32x4*>(orow + d);
-        if (beta) v += *p;
-        *p = v;
+        off[i][q] = rok && d < D ? (uint32_t)(((int64_t)lr * D + d) * 4) : kOob;
+      }
+    f32x4 old[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        old[i][q] = beta ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rs, off[i][q], 0, 0))
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = f32x4{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                              acc[i][j][4 * q + 3]} + old[i][q];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off[i][q], 0, 0);
       }
   }
   (void)N;

@@ -8,19 +8,25 @@
 //    no staging registers, no LDS store instructions, no register
 //    transposes.  Each lane loads whichever global chunk belongs at its LDS
 //    slot, which is how the layouts below get their swizzles.
-//  * 4 LDS stages of 32 K values each (32 KiB per stage, 128 KiB total),
-//    loaded 3 stages ahead; completion is tracked with explicit vmcnt waits.
-//  * Natural operands ([m][k], K contiguous) sit in LDS as [256 rows][64 B]:
-//    16-byte chunk c of row r at chunk c ^ ((r >> 1) & 3).  An MFMA fragment
+//  * Stages of 64 K values, so that every DMA instruction reads whole
+//    128-byte lines (8 rows of a natural operand, 2 k rows of a transposed
+//    one): measured on MI355X, loads of half lines reach about half the
+//    L2-to-CU rate of whole lines.  Two stage slots of 64 KiB (A + B).
+//  * Natural operands ([m][k], K contiguous) sit in LDS as [256 rows][128 B]:
+//    16-byte chunk c of row r at chunk c ^ (r & 7).  An MFMA fragment
 //    (8 K values of one row per lane) is one ds_read_b128.
 //  * Transposed operands ([k][m], M contiguous) sit in LDS as
-//    [32 k rows][512 B]: 32-byte segment s of row k at segment s ^ (k & 3).
+//    [64 k rows][512 B]: 32-byte segment s of row k at segment s ^ (k & 3).
 //    A fragment is two ds_read_b64_tr_b16: within each 16-lane group the
 //    hardware hands lane i the element (row kbase + e, column mbase + i),
 //    e = 0..3, when source lane j points at row kbase + j / 4, columns
 //    mbase + 4 (j % 4) .. +3 (measured lane layout of the instruction).
-//  * One barrier per stage, in the middle: the next stage's first fragments
-//    load while the current stage's second half of MFMAs runs.
+//  * One barrier per stage, before its last MFMA sub-step: the slot just
+//    read takes the DMAs of the stage after next, and the next stage's first
+//    fragments load while that sub-step runs.
+//  * Each workgroup also touches, one dword per 128-byte line, its share of
+//    the lines of the stage two ahead of the one being loaded, so those
+//    lines are in L2 when their DMAs are issued.
 //
 // The DMA instructions are inline assembly so that the compiler does not
 // wait for every outstanding DMA before each LDS read; the code below waits
@@ -34,11 +40,12 @@
 
 namespace flce {
 
-constexpr int kDmaStages = 4;
-constexpr int kDmaKStep = 32;                    // bf16 K values per stage
-constexpr int kDmaOpBytes = 256 * 64;            // one operand of one stage: 16 KiB
+constexpr int kDmaSlots = 2;
+constexpr int kDmaKStep = 64;                    // bf16 K values per stage
+constexpr int kDmaKs = kDmaKStep / 16;           // MFMA K sub-steps per stage
+constexpr int kDmaOpBytes = 256 * 128;           // one operand of one stage: 32 KiB
 constexpr int kDmaStageBytes = 2 * kDmaOpBytes;  // A + B
-constexpr int kDmaLdsBytes = kDmaStages * kDmaStageBytes;
+constexpr int kDmaLdsBytes = kDmaSlots * kDmaStageBytes;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
@@ -56,6 +63,22 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, uint32_t voff, __amdgpu
                : "memory", "m0");
 }
 
+// One lane's 4 bytes into LDS at m0 + 4 * lane: pulls the line holding them
+// into L2 ahead of the stage that loads it (the LDS target is a dummy area).
+__device__ __forceinline__ void dma4(uint32_t lds_base, uint32_t voff, __amdgpu_buffer_rsrc_t rs) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rs)
+               : "memory", "m0");
+}
+
+// The workgroups that run at the same time on one XCD and share an operand
+// block split the block's lines of a future stage `nshare` ways (a power of
+// two); this workgroup touches part `share`.
+struct L2Split {
+  int share, nshare;
+};
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -65,59 +88,67 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void barrier_raw() { asm volatile("s_barrier" ::: "memory"); }
 
 // ------------------------------------------------------------- loaders ----
-// Each wave issues 4 DMA instructions per operand per stage (16 per
-// workgroup = 16 KiB).  Offsets are fixed per lane; the descriptor base moves
-// along K.  Rows/columns outside the operand get an out-of-range offset, so
-// the hardware writes zeros into their LDS slots.
+// Each wave issues 8 DMA instructions per operand per stage (32 per
+// workgroup = 32 KiB), every instruction reading whole 128-byte lines.
+// Offsets are fixed per lane; the descriptor base moves along K.  Rows or
+// columns outside the operand get an out-of-range offset, so the hardware
+// writes zeros into their LDS slots.
 
-// natural [m][k]: instruction q of wave w covers tile rows 16 (4 w + q) .. +15;
-// lane L -> row 16 (4 w + q) + L / 4, LDS chunk L % 4, global chunk
-// (L % 4) ^ ((row >> 1) & 3).
+// natural [m][k]: instruction q of wave w covers tile rows 8 (8 w + q) .. +7
+// (128 bytes = 64 K values each); lane L -> row 8 (8 w + q) + L / 8, LDS
+// chunk L % 8, global chunk (L % 8) ^ (row % 8) = (L % 8) ^ (L / 8).
 struct DmaNatural {
-  uint32_t off[4];
-  bool rowok[4];
+  uint32_t off[8];
   int kc;                 // K element offset of this lane's chunk
   const char* base;       // element (m0, 0)
-  int64_t kext;
+  int64_t ld, kext, mrem;
   __device__ __forceinline__ void init(const Operand& op, int m0, int wave, int lane) {
     base = op.base + (int64_t)m0 * op.ld * 2;
+    ld = op.ld;
     kext = op.kext;
+    mrem = op.mext - m0;
+    const int c = (lane & 7) ^ (lane >> 3);
+    kc = c * 8;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 16 * (4 * wave + q) + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 1) & 3);
-      if (q == 0) kc = c * 8;
-      rowok[q] = (int64_t)m0 + row < op.mext;
-      off[q] = (uint32_t)(((int64_t)row * op.ld + c * 8) * 2);
+    for (int q = 0; q < 8; ++q) {
+      const int row = 8 * (8 * wave + q) + (lane >> 3);
+      off[q] = (int64_t)m0 + row < op.mext ? (uint32_t)(((int64_t)row * op.ld + c * 8) * 2) : kOob;
     }
   }
-  // chunk index depends on the row only through (row >> 1) & 3, which is the
-  // same for all q (row differs by multiples of 16) -> one kc for all q.
   __device__ __forceinline__ void issue(uint32_t lds_op, int k0, int wave) const {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)k0 * 2);
     const bool kin = k0 + kc < kext;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      dma16(lds_op + (4 * wave + q) * 1024, (kin && rowok[q]) ? off[q] : kOob, rs);
+    for (int q = 0; q < 8; ++q) dma16(lds_op + (8 * wave + q) * 1024, kin ? off[q] : kOob, rs);
+  }
+  // one 128-byte line per tile row: lane L touches row share * per + L % per
+  __device__ __forceinline__ void prefetch(uint32_t lds_dummy, int k0, L2Split sp, int lane,
+                                           bool on) const {
+    const int per = kTile / sp.nshare;
+    const int row = sp.share * per + (lane & (per - 1));
+    const bool ok = on && row < mrem && k0 < kext;
+    dma4(lds_dummy, ok ? (uint32_t)((int64_t)row * ld * 2) : kOob,
+         make_rsrc(base + (int64_t)k0 * 2));
   }
 };
 
-// transposed [k][m]: instruction q of wave w covers k rows 2 (4 w + q), +1;
-// lane L -> k row 2 (4 w + q) + L / 32, LDS segment (L % 32) / 2, half L % 2,
-// global segment ((L % 32) / 2) ^ (krow & 3).
+// transposed [k][m]: instruction q of wave w covers k rows 2 (8 w + q), +1
+// (512 bytes = 256 M values each); lane L -> k row 2 (8 w + q) + L / 32, LDS
+// segment (L % 32) / 2, half L % 2, global segment ((L % 32) / 2) ^ (krow % 4).
 struct DmaTransposed {
-  uint32_t off[4];
-  bool colok[4];
+  uint32_t off[8];
+  bool colok[8];
   const char* base;       // element (0, m0) of the stored [k][m] matrix
-  int64_t ld, kext;
+  int64_t ld, kext, mrem;
   int krow0;              // k row of instruction 0 for this lane
   __device__ __forceinline__ void init(const Operand& op, int m0, int wave, int lane) {
     base = op.base + (int64_t)m0 * 2;
     ld = op.ld;
     kext = op.kext;
-    krow0 = 8 * wave + (lane >> 5);
+    mrem = op.mext - m0;
+    krow0 = 16 * wave + (lane >> 5);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 8; ++q) {
       const int krow = krow0 + 2 * q;
       const int seg = ((lane & 31) >> 1) ^ (krow & 3);
       const int m = seg * 16 + (lane & 1) * 8;
@@ -128,10 +159,21 @@ struct DmaTransposed {
   __device__ __forceinline__ void issue(uint32_t lds_op, int k0, int wave) const {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)k0 * ld * 2);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 8; ++q) {
       const bool ok = colok[q] && (k0 + krow0 + 2 * q < kext);
-      dma16(lds_op + (4 * wave + q) * 1024, ok ? off[q] : kOob, rs);
+      dma16(lds_op + (8 * wave + q) * 1024, ok ? off[q] : kOob, rs);
     }
+  }
+  // four 128-byte lines per k row: lane L touches line li = share * per + L % per,
+  // k row li / 4, quarter li % 4
+  __device__ __forceinline__ void prefetch(uint32_t lds_dummy, int k0, L2Split sp, int lane,
+                                           bool on) const {
+    const int per = kTile / sp.nshare;
+    const int li = sp.share * per + (lane & (per - 1));
+    const int krow = li >> 2, quarter = li & 3;
+    const bool ok = on && k0 + krow < kext && quarter * 64 < mrem;
+    dma4(lds_dummy, ok ? (uint32_t)((int64_t)krow * ld * 2 + quarter * 128) : kOob,
+         make_rsrc(base + (int64_t)k0 * ld * 2));
   }
 };
 
@@ -140,34 +182,40 @@ template <> struct DmaLoader<false> : DmaNatural {};
 template <> struct DmaLoader<true> : DmaTransposed {};
 
 // ----------------------------------------------------------- fragments ----
-// Fragments of MFMA K sub-step ks (0 or 1) of a stage for the wave's 4 blocks.
+// Fragments of MFMA K sub-step KS (0..3) of a stage for the wave's 4 blocks.
 template <bool TRANS> struct FragReader;
 
+// natural: row r = wbase + 32 i + lane % 32, chunk 2 KS + lane / 32 stored at
+// chunk ^ (r % 8) = chunk ^ (lane % 8).
 template <> struct FragReader<false> {
-  int off[2];   // per ks: byte offset of this lane's chunk in its row
-  int row0;     // byte offset of row (wbase + lane % 32)
+  int off[kDmaKs];   // per KS: byte offset of this lane's fragment in block i = 0
   __device__ __forceinline__ void init(int wbase, int lane) {
     const int r = wbase + (lane & 31);
-    row0 = r * 64;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) off[ks] = ((2 * ks + (lane >> 5)) ^ ((r >> 1) & 3)) * 16;
+    for (int ks = 0; ks < kDmaKs; ++ks)
+      off[ks] = r * 128 + (((2 * ks + (lane >> 5)) ^ (lane & 7)) * 16);
   }
   template <int KS>
   __device__ __forceinline__ void read(const char* s, bf16x8 (&f)[4]) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      f[i] = *reinterpret_cast<const bf16x8*>(s + row0 + i * 32 * 64 + off[KS]);
+      f[i] = *reinterpret_cast<const bf16x8*>(s + off[KS] + i * 32 * 128);
   }
 };
 
+// transposed: lane l of 16-lane group g4 = l / 16 (k half h = l / 32, column
+// half g = g4 % 2, j = l % 16) points at k row 16 KS + 8 h + 4 e + j / 4,
+// columns wbase + 32 i + 16 g + 4 (j % 4) .. +3 (segment swizzled by k % 4);
+// the transposing read hands it (k = 16 KS + 8 h + 4 e + 0..3, column
+// wbase + 32 i + l % 32).
 template <> struct FragReader<true> {
-  int addr[2];  // per (i & 1): byte address of this lane's 8 bytes for ks 0, e 0, i 0/1
+  int addr[2];  // per (i & 1): byte address for KS 0, e 0
   __device__ __forceinline__ void init(int wbase, int lane) {
     const int h = lane >> 5, g = (lane >> 4) & 1, j = lane & 15;
-    const int krow = 8 * h + (j >> 2);          // + 16 ks + 4 e
+    const int krow = 8 * h + (j >> 2);          // + 16 KS + 4 e
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-      const int seg = (wbase >> 4) + 2 * ii + g;  // 16 m values per 32-byte segment
+      const int seg = (wbase >> 4) + 2 * ii + g;  // 16 columns per 32-byte segment
       addr[ii] = krow * 512 + ((seg ^ (krow & 3)) * 32) + (j & 3) * 8;
     }
   }
@@ -197,45 +245,51 @@ __device__ __forceinline__ void interleave_reads_mfma() {
   }
 }
 
-template <int KS>
-__device__ __forceinline__ void mfma_ks(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
-                                        const bf16x8 (&b)[4], bool fresh) {
+template <bool FRESH>
+__device__ __forceinline__ void mfma_group(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
+                                           const bf16x8 (&b)[4]) {
   const f32x16 zero = {};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j],
-                                                          (KS == 0 && fresh) ? zero : acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], FRESH ? zero : acc[i][j],
+                                                          0, 0, 0);
 }
 
-// acc = sum over active K steps (32 wide) of A[m][k] B[n][k] for the
+// acc = sum over active K steps (64 wide) of A[m][k] B[n][k] for the
 // 256 x 256 tile at (m0, n0); `active(s)` must agree across the workgroup.
+//
+// A stage (K = 64, four MFMA sub-steps ks0..ks3 of 16 MFMAs per wave) sits
+// in one of two LDS slots.  While sub-step k's MFMAs run, the fragments of
+// the sub-step after it are read.  Between ks2 and ks3 of a stage every wave
+// waits for its own DMAs of the next stage and for its reads of this slot,
+// then one barrier makes the next stage visible to all and frees this slot,
+// which immediately takes the DMAs of the stage after next.  The loop body
+// runs from ks1 of one stage to ks0 of the next, so the first MFMA group
+// (which starts from zero instead of the accumulators) sits before the loop.
 template <bool AT, bool BT, class Active>
 __device__ __forceinline__ void gemm_tile_dma(const Operand& A, const Operand& B, int m0, int n0,
                                               int nsteps, Active active,
-                                              f32x16 (&acc)[4][4], char* lds) {
+                                              f32x16 (&acc)[4][4], char* lds,
+                                              L2Split sa = {0, 8}, L2Split sb = {0, 4}) {
   active.prepare(nsteps);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto next_active = [&](int s) { return active.next(s, nsteps); };
-  int st[4];                         // the next 4 active steps (nsteps = none)
-  st[0] = next_active(0);
-  if (st[0] >= nsteps) {
+  int cur = active.next(0, nsteps);
+  if (cur >= nsteps) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     __syncthreads();
     return;
   }
-  st[1] = next_active(st[0] + 1);
-  st[2] = next_active(st[1] + 1);
-  st[3] = next_active(st[2] + 1);
+  int nxt = active.next(cur + 1, nsteps);
 
   DmaLoader<AT> la;
   DmaLoader<BT> lb;
@@ -250,56 +304,79 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand& A, const Operand& B
     la.issue(lbase + slot * kDmaStageBytes, step * kDmaKStep, wave);
     lb.issue(lbase + slot * kDmaStageBytes + kDmaOpBytes, step * kDmaKStep, wave);
   };
-  // prologue: up to 3 stages in flight
-  issue(0, st[0]);
-  if (st[1] < nsteps) issue(1, st[1]);
-  if (st[2] < nsteps) issue(2, st[2]);
-  // stage 0 landed (allow the 16 DMAs of stages 1, 2 to fly)
-  if (st[2] < nsteps) wait_vmcnt<16>();
-  else if (st[1] < nsteps) wait_vmcnt<8>();
-  else wait_vmcnt<0>();
+  // Wave 0 touches this workgroup's share of A's lines of a future step,
+  // wave 1 that of B; waves 2 and 3 issue the same instruction with every
+  // lane out of range (no memory access), so that every wave has the same
+  // number of loads in flight and the wait counts below hold for all.
+  const uint32_t ldummy = lbase + kDmaLdsBytes;
+  auto prefetch = [&](int step) {
+    const bool on = step < nsteps;
+    if (wave == 1) lb.prefetch(ldummy, step * kDmaKStep, sb, lane, on);
+    else la.prefetch(ldummy, step * kDmaKStep, sa, lane, on && wave == 0);
+  };
+  constexpr int kReads = 4 * (AT ? 2 : 1) + 4 * (BT ? 2 : 1);
+  issue(0, cur);
+  if (nxt < nsteps) {
+    issue(1, nxt);
+    prefetch(nxt + 1);
+    prefetch(nxt + 2);
+    wait_vmcnt<18>();      // the first stage (16 DMAs per wave per stage)
+  } else {
+    wait_vmcnt<0>();
+  }
   barrier_raw();
   bf16x8 a0[4], b0[4], a1[4], b1[4];
   fa.template read<0>(lds, a0);
   fb.template read<0>(lds + kDmaOpBytes, b0);
+  fa.template read<1>(lds, a1);
+  fb.template read<1>(lds + kDmaOpBytes, b1);
+  mfma_group<true>(acc, a0, b0);
+  interleave_reads_mfma<kReads>();
 
-  constexpr int kReads = 4 * (AT ? 2 : 1) + 4 * (BT ? 2 : 1);
-  bool fresh = true;
   int slot = 0;
-  // Steps with a successor run the straight-line body; the last step is
+  // Stages with a successor run the straight-line body; the last stage is
   // peeled so no control-flow merge sits between the next stage's fragment
-  // reads and this stage's second MFMA group (a merge would make the LDS
-  // wait count conservative and stall on those reads).
-  while (st[1] < nsteps) {
+  // reads and this stage's MFMAs (a merge would make the LDS wait count
+  // conservative and stall on those reads).
+  while (nxt < nsteps) {
     const char* s = lds + slot * kDmaStageBytes;
-    fa.template read<1>(s, a1);
-    fb.template read<1>(s + kDmaOpBytes, b1);
-    mfma_ks<0>(acc, a0, b0, fresh);
+    fa.template read<2>(s, a0);
+    fb.template read<2>(s + kDmaOpBytes, b0);
+    mfma_group<false>(acc, a1, b1);
     interleave_reads_mfma<kReads>();
-    fresh = false;
-    // the next stage landed: its DMAs were issued before those of the (up
-    // to) one stage behind it
-    if (st[2] < nsteps) wait_vmcnt<8>();
-    else wait_vmcnt<0>();
+    fa.template read<3>(s, a1);
+    fb.template read<3>(s + kDmaOpBytes, b1);
+    mfma_group<false>(acc, a0, b0);
+    interleave_reads_mfma<kReads>();
+    const int nn = active.next(nxt + 1, nsteps);   // the stage after next
+    // own DMAs of the next stage; only the latest line touch may still fly
+    // (loads complete in order, so every older one has landed too)
+    wait_vmcnt<1>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own reads of this slot
     barrier_raw();
-    // every wave is past stage slot-1: its buffer takes the step 3 ahead
-    if (st[3] < nsteps) issue((slot + 3) & 3, st[3]);
-    const char* sn = lds + ((slot + 1) & 3) * kDmaStageBytes;
+    if (nn < nsteps) issue(slot, nn);              // every wave is done with this slot
+    prefetch(nn + 2);
+    const char* sn = lds + (slot ^ 1) * kDmaStageBytes;
     fa.template read<0>(sn, a0);
     fb.template read<0>(sn + kDmaOpBytes, b0);
-    mfma_ks<1>(acc, a1, b1, false);
+    mfma_group<false>(acc, a1, b1);
     interleave_reads_mfma<kReads>();
-    st[1] = st[2];
-    st[2] = st[3];
-    st[3] = st[3] < nsteps ? next_active(st[3] + 1) : nsteps;
-    slot = (slot + 1) & 3;
+    fa.template read<1>(sn, a1);
+    fb.template read<1>(sn + kDmaOpBytes, b1);
+    mfma_group<false>(acc, a0, b0);
+    interleave_reads_mfma<kReads>();
+    nxt = nn;
+    slot ^= 1;
   }
   {
     const char* s = lds + slot * kDmaStageBytes;
-    fa.template read<1>(s, a1);
-    fb.template read<1>(s + kDmaOpBytes, b1);
-    mfma_ks<0>(acc, a0, b0, fresh);
-    mfma_ks<1>(acc, a1, b1, false);
+    fa.template read<2>(s, a0);
+    fb.template read<2>(s + kDmaOpBytes, b0);
+    mfma_group<false>(acc, a1, b1);
+    fa.template read<3>(s, a1);
+    fb.template read<3>(s + kDmaOpBytes, b1);
+    mfma_group<false>(acc, a0, b0);
+    mfma_group<false>(acc, a1, b1);
   }
   acc_fence(acc);
   __syncthreads();   // LDS may be reused by the caller

@@ -28,7 +28,8 @@ namespace {
 
 constexpr uint64_t kDefaultBudget = 64ull << 20;
 constexpr int kFilterBlock = 64;
-constexpr int kMaxBand = 4096;
+constexpr int kMaxBandRows = 4096;    // NS: token rows of a backward band
+constexpr int kMaxBandVocab = 8192;   // VS: the filter's K-skip masks cover K <= 8192
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -93,8 +94,12 @@ int make_plan(const flce_desc* d, Plan& p) {
   p.Tv = int(cdiv(p.V, flce::kTile));
   const int64_t Npad = cdiv(std::max<int64_t>(p.N, 1), 256) * 256;
   p.nblk = int(cdiv(std::max<int64_t>(p.N, 1), flce::kCombineRows));   // one per combine block
-  p.NS = int(std::min<int64_t>(kMaxBand, Npad));
-  p.VS = int(std::min<int64_t>(kMaxBand, cdiv(p.V, 256) * 256));
+  // The band is as large as the budget allows: every band costs a dZ launch
+  // and a gradient launch, and the fp32 read-modify-write of dH and dW per
+  // step scales with 1 / NS + 1 / VS.  NS is capped first (its tiles fill
+  // the machine already at 4096 rows); VS then grows in steps of 256.
+  p.NS = int(std::min<int64_t>(kMaxBandRows, Npad));
+  p.VS = int(std::min<int64_t>(kMaxBandVocab, cdiv(p.V, 256) * 256));
   const uint64_t budget = d->ws_budget_bytes ? d->ws_budget_bytes : kDefaultBudget;
   for (;;) {
     p.frows = p.NS / kFilterBlock;
@@ -104,9 +109,20 @@ int make_plan(const flce_desc* d, Plan& p) {
     p.NF = int(std::max<int64_t>(256, std::min<int64_t>(Npad, fit)));
     if (layout(p) <= budget) break;
     if (p.NS <= 256 && p.VS <= 256) return FLCE_E_WORKSPACE;
-    if (p.VS >= p.NS) p.VS = std::max(256, (p.VS / 2 + 255) / 256 * 256);
+    if (p.VS > p.NS) p.VS -= 256;
+    else if (p.VS == p.NS) p.VS = std::max(256, (p.VS / 2 + 255) / 256 * 256);
     else p.NS = std::max(256, (p.NS / 2 + 255) / 256 * 256);
   }
+  // Same band counts, sizes spread evenly (no thin last band); never larger.
+  p.NS = int(cdiv(cdiv(std::max<int64_t>(p.N, 1), cdiv(std::max<int64_t>(p.N, 1), p.NS)), 256) * 256);
+  p.VS = int(cdiv(cdiv(p.V, cdiv(p.V, p.VS)), 256) * 256);
+  p.frows = p.NS / kFilterBlock;
+  p.fcols = p.VS / kFilterBlock;
+  {
+    const int64_t fit = int64_t(size_t(p.NS) * p.VS * p.es / (size_t(8) * p.Tv)) / 256 * 256;
+    p.NF = int(std::max<int64_t>(256, std::min<int64_t>(Npad, fit)));
+  }
+  layout(p);
   p.nbf = int(cdiv(std::max<int64_t>(p.N, 1), p.NF));
   p.nbn = int(cdiv(std::max<int64_t>(p.N, 1), p.NS));
   p.nbv = int(cdiv(p.V, p.VS));

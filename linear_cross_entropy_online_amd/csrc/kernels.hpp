@@ -487,26 +487,41 @@ template <int STEP>
 struct SkipRowsOfFlags {
   static_assert(STEP == 64 || STEP == 32, "step width");
   static constexpr int kShift = STEP == 64 ? 0 : 1;   // log2(steps per 64-block)
+  static constexpr int kMaxBlocks = 128;              // K <= 8192
   const uint8_t* base;     // first of the four flags of 64-block 0
   int step_stride;         // bytes between consecutive 64-blocks
-  uint64_t mask = 0;       // bit b: 64-block b is active
+  uint64_t lo = 0, hi = 0; // bit b of (hi:lo): 64-block b is active
   __device__ __forceinline__ void prepare(int nsteps) {
-    const int nb = (nsteps + (1 << kShift) - 1) >> kShift;   // 64-blocks (<= 64)
-    uint64_t m = 0;
-    for (int b = 0; b < nb; ++b) {
+    const int nb = (nsteps + (1 << kShift) - 1) >> kShift;
+    uint64_t m0 = 0, m1 = 0;
+    for (int b = 0; b < nb && b < 64; ++b) {
       const uint32_t f = *reinterpret_cast<const uint32_t*>(base + b * step_stride);
-      m |= (uint64_t)(f != 0x01010101u) << b;
+      m0 |= (uint64_t)(f != 0x01010101u) << b;
     }
-    mask = m;
+    for (int b = 64; b < nb && b < kMaxBlocks; ++b) {
+      const uint32_t f = *reinterpret_cast<const uint32_t*>(base + b * step_stride);
+      m1 |= (uint64_t)(f != 0x01010101u) << (b - 64);
+    }
+    lo = m0;
+    hi = m1;
   }
-  __device__ __forceinline__ bool operator()(int s) const { return (mask >> (s >> kShift)) & 1; }
+  __device__ __forceinline__ bool operator()(int s) const {
+    const int b = s >> kShift;
+    return ((b < 64 ? lo >> b : hi >> (b - 64)) & 1) != 0;
+  }
   // first active step >= s (nsteps if none)
   __device__ __forceinline__ int next(int s, int nsteps) const {
     const int b = s >> kShift;
-    if (b >= 64) return nsteps;
-    const uint64_t rest = mask >> b;
-    if (rest == 0) return nsteps;
-    const int nb = b + __builtin_ctzll(rest);
+    int nb;
+    if (b < 64 && (lo >> b) != 0) {
+      nb = b + __builtin_ctzll(lo >> b);
+    } else {
+      const int c = b < 64 ? 0 : b - 64;
+      if (c >= 64) return nsteps;
+      const uint64_t rest = hi >> c;
+      if (rest == 0) return nsteps;
+      nb = 64 + c + __builtin_ctzll(rest);
+    }
     const int ns = nb == b ? s : (nb << kShift);
     return ns < nsteps ? ns : nsteps;
   }
@@ -525,15 +540,20 @@ bwd_grad_kernel(const T* __restrict__ H, const T* __restrict__ W, const T* __res
                 float* __restrict__ dH, float* __restrict__ dW, int N, int D, int V,
                 BandArgs band, int T3n, int T2n, int Td, int beta_h, int beta_w) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  // The contraction with the longer K (dH^T: band vocabulary, dW^T: band
+  // rows) is dispatched first on every XCD.
+  const int T3 = Td * T3n, T2 = Td * T2n;
+  const bool h_first = band.vs_cur >= band.ns_cur;
+  const int t = xcd_remap_split(blockIdx.x, gridDim.x, h_first ? T3 : T2);
+  const bool is_h = h_first ? t < T3 : t >= T2;
+  const int local = h_first ? (is_h ? t : t - T3) : (is_h ? t - T2 : t);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   f32x16 acc[4][4];
   float* out;
   int rvalid, beta, td, tr;
-  const int T3 = Td * T3n;
-  if (t < T3) {
-    grouped_tile(t, Td, T3n, 4, td, tr);   // d tile, band row tile
+  if (is_h) {
+    grouped_tile(local, Td, T3n, 4, td, tr);   // d tile, band row tile
     const Operand A{reinterpret_cast<const char*>(W + (int64_t)band.vb0 * D), D, D, band.vs_cur};
     const int kpad = (band.vs_cur + kTile - 1) / kTile * kTile;
     const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T3n * kTile, kpad};
@@ -547,7 +567,7 @@ bwd_grad_kernel(const T* __restrict__ H, const T* __restrict__ W, const T* __res
     rvalid = band.ns_cur;
     beta = beta_h;
   } else {
-    grouped_tile(t - T3, Td, T2n, 4, td, tr);   // d tile, band vocabulary tile
+    grouped_tile(local, Td, T2n, 4, td, tr);   // d tile, band vocabulary tile
     const Operand A{reinterpret_cast<const char*>(H + (int64_t)band.nb0 * D), D, D, band.ns_cur};
     const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2n * kTile, band.ns_cur};
     if constexpr (FILTER) {

@@ -353,6 +353,20 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
   return x * q + (x < rem ? x : rem) + idx;
 }
 
+// As xcd_remap, for a grid whose tiles [0, T1) are longer than the rest:
+// XCD x gets an even share of each kind as two contiguous ranges and is sent
+// its long tiles first, so that no XCD is left holding most of the long work.
+__device__ __forceinline__ int xcd_remap_split(int b, int G, int T1) {
+  const int x = b & 7, idx = b >> 3;
+  const int q = G >> 3, rem = G & 7;
+  const int q1 = T1 >> 3, r1 = T1 & 7;
+  const int nl = q1 + (x < r1 ? 1 : 0);
+  const int l0 = x * q1 + (x < r1 ? x : r1);
+  if (idx < nl) return l0 + idx;
+  const int s0 = x * q + (x < rem ? x : rem) - l0;   // short tiles of the XCDs before x
+  return T1 + s0 + (idx - nl);
+}
+
 // Tile id t -> (tm, tn) in a TM x TN grid, visiting GM tile rows at a time.
 __device__ __forceinline__ void grouped_tile(int t, int TM, int TN, int GM, int& tm, int& tn) {
   const int per = GM * TN;

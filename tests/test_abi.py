@@ -136,11 +136,13 @@ def test_budget_shrinks_bands_and_reports_overflow():
 
 
 def test_extra_memory_is_bounded_by_rows_plus_tile():
-    """Workspace grows with N (per-row partials) but not with V beyond one band."""
+    """Workspace grows with N (per-row partials) but not with V: the dZ band
+    fills the budget whatever V is (its width only rounds to even bands)."""
     a = L.flce_plan(8192, 2048, 151552)["ws_bytes"]
     b = L.flce_plan(8192, 2048, 4 * 151552)["ws_bytes"]
     c = L.flce_plan(131072, 2048, 151552)["ws_bytes"]
-    assert a == b
+    assert max(a, b) <= 64 * MiB
+    assert abs(a - b) <= 4096 * 256 * 2 + MiB      # at most one 256-wide band step
     assert c - a < 16 * 131072 + MiB
 
 

@@ -38,6 +38,25 @@ def parse():
     return p.parse_args()
 
 
+def backward_flops_by_class(plan, N, D, V):
+    """Algorithmic flops of the backward launch classes, following the
+    library's launch sequence: launch k holds the dZ tiles of band k
+    (2 ns vs D) and the gradient tiles of band k - 1 (4 ns vs D); the first
+    launch is class bwd_dz, the last bwd_grad, the others bwd_band."""
+    NS, VS, nbn, nbv = (plan["band_rows"], plan["band_vocab"], plan["n_bands_rows"],
+                        plan["n_bands_vocab"])
+    bands = [(min(NS, N - bn * NS), min(VS, V - bv * VS)) for bn in range(nbn) for bv in range(nbv)]
+    out = {"bwd_dz": 0.0, "bwd_grad": 0.0, "bwd_band": 0.0}
+    nb = len(bands)
+    for k in range(nb + 1):
+        cls = "bwd_dz" if k == 0 else ("bwd_grad" if k == nb else "bwd_band")
+        if k < nb:
+            out[cls] += 2.0 * bands[k][0] * bands[k][1] * D
+        if k > 0:
+            out[cls] += 4.0 * bands[k - 1][0] * bands[k - 1][1] * D
+    return out
+
+
 def cpu_baseline(H, W, y, reduction, rows):
     """The fp64 oracle, as it stands, on the first `rows` token rows of the
     same workload (full vocabulary): loss, dH and the rows' dW contribution."""
@@ -127,10 +146,11 @@ def main():
                                  "ms_per_step": t / args.steps}
         print(f"bench: kernels {json.dumps(kernels)}", file=sys.stderr, flush=True)
 
-    # algorithmic flops per launch of each contraction class, for this plan
+    # algorithmic flops per step of each contraction class, for this plan
     NS, VS = plan["band_rows"], plan["band_vocab"]
     n_bands = plan["n_bands_rows"] * plan["n_bands_vocab"]
-    flops_per_step = {"fwd_lse": 2.0 * ndv, "bwd_dz": 2.0 * ndv, "bwd_grad": 4.0 * ndv}
+    flops_per_step = backward_flops_by_class(plan, N, D, V)
+    flops_per_step["fwd_lse"] = 2.0 * ndv
     roofline = None
     if kernels:
         dom = max((k for k in kernels if k in flops_per_step), key=lambda k: kernels[k]["ms_per_step"])

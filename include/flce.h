@@ -98,7 +98,7 @@ typedef struct flce_plan_info {
   int32_t fwd_workgroups;  /* forward grid of one band (256 x 256 logits tiles) */
   int32_t tile;            /* output tile edge of every contraction (256)      */
   int32_t filter_block;    /* edge of a filter block (64)                      */
-  int64_t dz_bytes;        /* bytes of the staged dZ band inside ws            */
+  int64_t dz_bytes;        /* bytes of one of the two staged dZ band buffers   */
 } flce_plan_info;
 
 /* Exact workspace size for *d (the maximum over the three compute entry
@@ -123,7 +123,8 @@ int flce_forward(const flce_desc* d, const void* H, const void* W, const int64_t
  * dloss is a device pointer: [1] for FLCE_MEAN / FLCE_SUM, [N] for FLCE_NONE;
  * NULL means an upstream gradient of 1.  The logits are recomputed block by
  * block, dZ is staged in ws one band at a time (bf16 for bf16 inputs, float
- * for float inputs) and contracted into dH and dW (CCE Alg. 4 structure). */
+ * for float inputs; two band buffers, one written while the other is
+ * contracted) and contracted into dH and dW (CCE Alg. 4 structure). */
 int flce_backward(const flce_desc* d, const void* H, const void* W, const int64_t* y,
                   const float* lse, const float* dloss,
                   float* dH, float* dW,
@@ -147,10 +148,13 @@ enum {
   FLCE_K_FWD_LSE = 0,     /* forward contraction + online max/sum-exp        */
   FLCE_K_LSE_COMBINE = 1, /* per-row merge of partials, loss rows            */
   FLCE_K_FINALIZE = 2,    /* scalar loss / row scale                         */
-  FLCE_K_BWD_DZ = 3,      /* logits recompute + dZ band                      */
-  FLCE_K_BWD_GRAD = 4,    /* dH += dZ W_band and dW_band (+)= dZ^T H_band    */
+  FLCE_K_BWD_DZ = 3,      /* first backward launch: dZ of band 0 only        */
+  FLCE_K_BWD_GRAD = 4,    /* last backward launch: dH, dW of the last band   */
   FLCE_K_AUX = 5,         /* small fills                                     */
-  FLCE_K_COUNT = 6
+  FLCE_K_BWD_BAND = 6,    /* other backward launches: dH += dZ W_band and
+                             dW_band (+)= dZ^T H_band of band k - 1 together
+                             with the logits recompute + dZ of band k        */
+  FLCE_K_COUNT = 7
 };
 
 /* Launch timing recorded while desc->flags has FLCE_FLAG_PROFILE.  Each

@@ -22,8 +22,8 @@ import ctypes
 import torch
 
 from . import _abi
-from ._abi import (FLCE_BF16, FLCE_F32, FLCE_FLAG_PROFILE, FLCE_K_AUX, FLCE_K_BWD_DZ,
-                   FLCE_K_BWD_GRAD, FLCE_K_COUNT, FLCE_K_FINALIZE, FLCE_K_FWD_LSE,
+from ._abi import (FLCE_BF16, FLCE_F32, FLCE_FLAG_PROFILE, FLCE_K_AUX, FLCE_K_BWD_BAND,
+                   FLCE_K_BWD_DZ, FLCE_K_BWD_GRAD, FLCE_K_COUNT, FLCE_K_FINALIZE, FLCE_K_FWD_LSE,
                    FLCE_K_LSE_COMBINE, FLCE_MEAN, FLCE_NONE, FLCE_SUM, FlceError, lib)
 
 __all__ = ["flce_workspace_bytes", "flce_plan", "flce_forward", "flce_backward",
@@ -34,7 +34,7 @@ __all__ = ["flce_workspace_bytes", "flce_plan", "flce_forward", "flce_backward",
 _RED = {"mean": FLCE_MEAN, "sum": FLCE_SUM, "none": FLCE_NONE}
 KERNEL_CLASSES = {"fwd_lse": FLCE_K_FWD_LSE, "lse_combine": FLCE_K_LSE_COMBINE,
                   "finalize": FLCE_K_FINALIZE, "bwd_dz": FLCE_K_BWD_DZ,
-                  "bwd_grad": FLCE_K_BWD_GRAD, "aux": FLCE_K_AUX}
+                  "bwd_grad": FLCE_K_BWD_GRAD, "aux": FLCE_K_AUX, "bwd_band": FLCE_K_BWD_BAND}
 
 
 def _dtype_code(t: torch.dtype) -> int:

@@ -13,7 +13,7 @@ FLCE_BF16, FLCE_F32 = 0, 1
 FLCE_MEAN, FLCE_SUM, FLCE_NONE = 0, 1, 2
 FLCE_FLAG_PROFILE = 1
 (FLCE_K_FWD_LSE, FLCE_K_LSE_COMBINE, FLCE_K_FINALIZE, FLCE_K_BWD_DZ, FLCE_K_BWD_GRAD,
- FLCE_K_AUX, FLCE_K_COUNT) = range(7)
+ FLCE_K_AUX, FLCE_K_BWD_BAND, FLCE_K_COUNT) = range(8)
 
 # Every function include/flce.h declares (checked against the header by a CPU test).
 EXPORTS = ["flce_workspace_bytes", "flce_plan", "flce_forward", "flce_backward",

@@ -6,10 +6,12 @@
 //     fwd_lse_kernel     grid = ceil(V/256) x ceil(NF/256) logits tiles
 //     lse_combine_kernel grid = ceil(NF/256)
 //   finalize_kernel      1 block
-//   for each band of NS token rows:
-//     for each band of VS vocabulary rows:
-//       bwd_dz_kernel    grid = ceil(VS/256) x ceil(NS/256)
-//       bwd_grad_kernel  grid = ceil(D/256) x ceil(NS/256) + ceil(D/256) x ceil(VS/256)
+//   bands k = 0 .. nb-1 of NS token rows x VS vocabulary rows (rows outer):
+//     bwd_band_kernel    launch k: the gradient tiles of band k - 1
+//                        (ceil(D/256) x ceil(NS/256) for dH^T + ceil(D/256) x
+//                        ceil(VS/256) for dW^T, reading dZ buffer (k-1) % 2)
+//                        and the dZ tiles of band k (ceil(VS/256) x
+//                        ceil(NS/256), writing buffer k % 2); nb + 1 launches
 // dH of a token band accumulates over the vocabulary bands and dW of a
 // vocabulary band over the token bands; the first contribution stores, the
 // rest add, all in stream order, so the result is deterministic.
@@ -43,7 +45,9 @@ struct Plan {
   int nbn, nbv;        // backward band counts
   int frows, fcols;    // flag grid of a backward band
   int nblk;            // combine blocks (16 rows each)
-  size_t big;          // bytes shared by the forward partials and the dZ band
+  size_t big;          // bytes shared by the forward partials and the dZ buffers
+  size_t dz_bytes;     // one dZ band buffer
+  size_t flag_bytes;   // one flag grid
   size_t off_zy, off_bsum, off_bcnt, off_flags, off_flagsT, off_big, total;
 };
 
@@ -59,10 +63,11 @@ int validate(const flce_desc* d) {
   return FLCE_OK;
 }
 
-// Workspace: Header | zy [N] | block sums | block counts | flags | flagsT | big,
-// where `big` holds either the forward partials of one band
-// (2 x Tv x NF floats) or the backward dZ band (NS x VS elements): the
-// forward's partials are consumed before the first dZ band is written.
+// Workspace: Header | zy [N] | block sums | block counts | flags x 2 |
+// flagsT x 2 | big, where `big` holds either the forward partials of one band
+// (2 x Tv x NF floats) or two backward dZ band buffers (NS x VS elements
+// each; one is written while the other is contracted): the forward's
+// partials are consumed before the first dZ band is written.
 size_t layout(Plan& p) {
   size_t o = 256;  // Header
   const size_t N = size_t(p.N);
@@ -72,15 +77,26 @@ size_t layout(Plan& p) {
   o = align256(o + size_t(p.nblk) * 8);
   p.off_bcnt = o;
   o = align256(o + size_t(p.nblk) * 4);
+  p.flag_bytes = align256(size_t(p.frows) * p.fcols);
   p.off_flags = o;
-  o = align256(o + size_t(p.frows) * p.fcols);
+  o += 2 * p.flag_bytes;
   p.off_flagsT = o;
-  o = align256(o + size_t(p.frows) * p.fcols);
+  o += 2 * p.flag_bytes;
   p.off_big = o;
-  p.big = std::max(size_t(p.NS) * p.VS * p.es, size_t(2) * p.Tv * p.NF * 4);
+  p.dz_bytes = align256(size_t(p.NS) * p.VS * p.es);
+  p.big = std::max(2 * p.dz_bytes, size_t(2) * p.Tv * p.NF * 4);
   o = align256(o + p.big);
   p.total = o;
   return o;
+}
+
+// Smallest multiple of 256 that splits n into as few parts as parts of at
+// most `cap` (a multiple of 256) would.
+int64_t even_split(int64_t n, int64_t cap) {
+  for (int64_t parts = cdiv(n, cap);; ++parts) {
+    const int64_t sz = cdiv(cdiv(n, parts), 256) * 256;
+    if (sz <= cap) return sz;
+  }
 }
 
 int make_plan(const flce_desc* d, Plan& p) {
@@ -94,32 +110,45 @@ int make_plan(const flce_desc* d, Plan& p) {
   p.Tv = int(cdiv(p.V, flce::kTile));
   const int64_t Npad = cdiv(std::max<int64_t>(p.N, 1), 256) * 256;
   p.nblk = int(cdiv(std::max<int64_t>(p.N, 1), flce::kCombineRows));   // one per combine block
-  // The band is as large as the budget allows: every band costs a dZ launch
-  // and a gradient launch, and the fp32 read-modify-write of dH and dW per
-  // step scales with 1 / NS + 1 / VS.  NS is capped first (its tiles fill
-  // the machine already at 4096 rows); VS then grows in steps of 256.
-  p.NS = int(std::min<int64_t>(kMaxBandRows, Npad));
-  p.VS = int(std::min<int64_t>(kMaxBandVocab, cdiv(p.V, 256) * 256));
+  // The band is as large as the budget allows: every band costs a launch,
+  // and the fp32 read-modify-write of dH and dW per step scales with
+  // 1 / NS + 1 / VS.  For NS from its cap (its tiles fill the machine at 4096
+  // rows) down by halves, VS is the widest multiple of 256 that fits; the
+  // first NS whose VS is at least NS / 2 is taken.
   const uint64_t budget = d->ws_budget_bytes ? d->ws_budget_bytes : kDefaultBudget;
-  for (;;) {
+  const int vs_cap = int(std::min<int64_t>(kMaxBandVocab, cdiv(p.V, 256) * 256));
+  auto fits = [&](int ns, int vs) {
+    p.NS = ns;
+    p.VS = vs;
     p.frows = p.NS / kFilterBlock;
     p.fcols = p.VS / kFilterBlock;
-    // forward band: as many token rows as fit in the dZ band's bytes (>= 256)
-    const int64_t fit = int64_t(size_t(p.NS) * p.VS * p.es / (size_t(8) * p.Tv)) / 256 * 256;
+    // forward band: as many token rows as fit in the dZ buffers' bytes (>= 256)
+    const int64_t fit = int64_t(size_t(p.NS) * p.VS * p.es / (size_t(4) * p.Tv)) / 256 * 256;
     p.NF = int(std::max<int64_t>(256, std::min<int64_t>(Npad, fit)));
-    if (layout(p) <= budget) break;
-    if (p.NS <= 256 && p.VS <= 256) return FLCE_E_WORKSPACE;
-    if (p.VS > p.NS) p.VS -= 256;
-    else if (p.VS == p.NS) p.VS = std::max(256, (p.VS / 2 + 255) / 256 * 256);
-    else p.NS = std::max(256, (p.NS / 2 + 255) / 256 * 256);
+    return layout(p) <= budget;
+  };
+  int ns_best = 0, vs_best = 0;
+  for (int ns = int(std::min<int64_t>(kMaxBandRows, Npad));; ns = std::max(256, ns / 2 / 256 * 256)) {
+    int vs = vs_cap;
+    while (vs > 256 && !fits(ns, vs)) vs -= 256;
+    if (fits(ns, vs) && (vs >= ns / 2 || vs == vs_cap || ns == 256)) {
+      ns_best = ns;
+      vs_best = vs;
+      break;
+    }
+    if (ns == 256) break;
   }
-  // Same band counts, sizes spread evenly (no thin last band); never larger.
-  p.NS = int(cdiv(cdiv(std::max<int64_t>(p.N, 1), cdiv(std::max<int64_t>(p.N, 1), p.NS)), 256) * 256);
-  p.VS = int(cdiv(cdiv(p.V, cdiv(p.V, p.VS)), 256) * 256);
+  if (ns_best == 0) return FLCE_E_WORKSPACE;
+  p.NS = ns_best;
+  p.VS = vs_best;
+  // Band sizes spread evenly over the fewest bands whose rounded size still
+  // fits (no thin last band); never larger than what was fitted.
+  p.NS = int(even_split(std::max<int64_t>(p.N, 1), p.NS));
+  p.VS = int(even_split(p.V, p.VS));
   p.frows = p.NS / kFilterBlock;
   p.fcols = p.VS / kFilterBlock;
   {
-    const int64_t fit = int64_t(size_t(p.NS) * p.VS * p.es / (size_t(8) * p.Tv)) / 256 * 256;
+    const int64_t fit = int64_t(size_t(p.NS) * p.VS * p.es / (size_t(4) * p.Tv)) / 256 * 256;
     p.NF = int(std::max<int64_t>(256, std::min<int64_t>(Npad, fit)));
   }
   layout(p);
@@ -169,8 +198,8 @@ struct Ws {
   float *pm, *zy;        // pm: forward partials, aliasing the dZ band
   double* bsum;
   int* bcnt;
-  uint8_t *flags, *flagsT;
-  void* dz;
+  uint8_t *flags[2], *flagsT[2];
+  char* dz[2];
 };
 
 Ws carve(const Plan& p, void* ws) {
@@ -181,9 +210,11 @@ Ws carve(const Plan& p, void* ws) {
   w.zy = reinterpret_cast<float*>(b + p.off_zy);
   w.bsum = reinterpret_cast<double*>(b + p.off_bsum);
   w.bcnt = reinterpret_cast<int*>(b + p.off_bcnt);
-  w.flags = reinterpret_cast<uint8_t*>(b + p.off_flags);
-  w.flagsT = reinterpret_cast<uint8_t*>(b + p.off_flagsT);
-  w.dz = b + p.off_big;
+  for (int k = 0; k < 2; ++k) {
+    w.flags[k] = reinterpret_cast<uint8_t*>(b + p.off_flags + k * p.flag_bytes);
+    w.flagsT[k] = reinterpret_cast<uint8_t*>(b + p.off_flagsT + k * p.flag_bytes);
+    w.dz[k] = b + p.off_big + k * p.dz_bytes;
+  }
   return w;
 }
 
@@ -215,43 +246,68 @@ int run_forward(const flce_desc* d, const Plan& p, const void* H, const void* W,
   return FLCE_OK;
 }
 
+flce::BandArgs band_args(const Plan& p, int k) {
+  const int bn = k / p.nbv, bv = k % p.nbv;
+  flce::BandArgs band;
+  band.nb0 = bn * p.NS;
+  band.ns_cur = int(std::min<int64_t>(p.NS, p.N - band.nb0));
+  band.vb0 = bv * p.VS;
+  band.vs_cur = int(std::min<int64_t>(p.VS, p.V - band.vb0));
+  band.ldz = p.VS;
+  band.frows = p.frows;
+  band.fcols = p.fcols;
+  return band;
+}
+
+// Bands k = 0 .. nb-1 (token-row band outer, vocabulary band inner).  Launch
+// k runs the gradient tiles of band k - 1 and the dZ tiles of band k, with
+// band k's dZ in buffer k % 2: the first launch only makes dZ, the last only
+// contracts.  Launches on one stream run in order, so band k - 1's dZ is
+// complete before its gradient tiles start, and buffer k % 2 is no longer
+// read (band k - 2's gradients ran in launch k - 1) when band k writes it.
 template <typename T>
 int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, const int64_t* y,
               const float* lse, const float* dloss_rows, float* dH, float* dW, const Ws& w,
               bool prof, hipStream_t s) {
   const int N = int(p.N), D = int(p.D), V = int(p.V);
   const int Td = int(cdiv(D, flce::kTile));
-  for (int bn = 0; bn < p.nbn; ++bn) {
-    for (int bv = 0; bv < p.nbv; ++bv) {
-      flce::BandArgs band;
-      band.nb0 = bn * p.NS;
-      band.ns_cur = int(std::min<int64_t>(p.NS, p.N - band.nb0));
-      band.vb0 = bv * p.VS;
-      band.vs_cur = int(std::min<int64_t>(p.VS, p.V - band.vb0));
-      band.ldz = p.VS;
-      band.frows = p.frows;
-      band.fcols = p.fcols;
+  const int nb = p.nbn * p.nbv;
+  for (int k = 0; k <= nb; ++k) {
+    flce::DzArgs<T> da{};
+    flce::GradArgs<T> ga{};
+    int g_long = 0, g_grad = 0, g_dz = 0, h_first = 1;
+    if (k < nb) {
+      const flce::BandArgs band = band_args(p, k);
       const int TMv = int(cdiv(band.vs_cur, flce::kTile));
       const int TNn = int(cdiv(band.ns_cur, flce::kTile));
-      FLCE_TRY(launch(FLCE_K_BWD_DZ, prof, s, [&] {
-        flce::bwd_dz_kernel<T><<<dim3(TMv * TNn), dim3(flce::kThreads), 0, s>>>(
-            static_cast<const T*>(H), static_cast<const T*>(W), y, lse, dloss_rows, w.hdr, N, D, V,
-            d->ignore_index, d->reduction, d->filter_eps, band, TMv, TNn, static_cast<T*>(w.dz),
-            w.flags, w.flagsT);
-      }));
-      FLCE_TRY(launch(FLCE_K_BWD_GRAD, prof, s, [&] {
-        const dim3 grid(TNn * Td + TMv * Td), block(flce::kThreads);
-        const int bh = bv > 0 ? 1 : 0, bw = bn > 0 ? 1 : 0;
-        if (d->filter_eps > 0.f)
-          flce::bwd_grad_kernel<T, true><<<grid, block, 0, s>>>(
-              static_cast<const T*>(H), static_cast<const T*>(W), static_cast<const T*>(w.dz),
-              w.flags, w.flagsT, dH, dW, N, D, V, band, TNn, TMv, Td, bh, bw);
-        else
-          flce::bwd_grad_kernel<T, false><<<grid, block, 0, s>>>(
-              static_cast<const T*>(H), static_cast<const T*>(W), static_cast<const T*>(w.dz),
-              w.flags, w.flagsT, dH, dW, N, D, V, band, TNn, TMv, Td, bh, bw);
-      }));
+      da = flce::DzArgs<T>{static_cast<const T*>(H), static_cast<const T*>(W), y, lse, dloss_rows,
+                           w.hdr, N, D, V, d->ignore_index, d->reduction, d->filter_eps, band,
+                           TMv, TNn, reinterpret_cast<T*>(w.dz[k & 1]), w.flags[k & 1],
+                           w.flagsT[k & 1]};
+      g_dz = TMv * TNn;
     }
+    if (k > 0) {
+      const flce::BandArgs band = band_args(p, k - 1);
+      const int T2n = int(cdiv(band.vs_cur, flce::kTile));
+      const int T3n = int(cdiv(band.ns_cur, flce::kTile));
+      const int bn = (k - 1) / p.nbv, bv = (k - 1) % p.nbv;
+      ga = flce::GradArgs<T>{static_cast<const T*>(H), static_cast<const T*>(W),
+                             reinterpret_cast<const T*>(w.dz[(k - 1) & 1]), w.flags[(k - 1) & 1],
+                             w.flagsT[(k - 1) & 1], dH, dW, N, D, V, band, T3n, T2n, Td,
+                             bv > 0 ? 1 : 0, bn > 0 ? 1 : 0};
+      // the contraction with the longer K (dH^T: band vocabulary, dW^T: band rows) first
+      h_first = band.vs_cur >= band.ns_cur ? 1 : 0;
+      g_long = Td * (h_first ? T3n : T2n);
+      g_grad = Td * (T3n + T2n);
+    }
+    const int cls = k == 0 ? FLCE_K_BWD_DZ : (k == nb ? FLCE_K_BWD_GRAD : FLCE_K_BWD_BAND);
+    FLCE_TRY(launch(cls, prof, s, [&] {
+      const dim3 grid(g_grad + g_dz), block(flce::kThreads);
+      if (d->filter_eps > 0.f)
+        flce::bwd_band_kernel<T, true><<<grid, block, 0, s>>>(ga, da, g_long, g_grad, h_first);
+      else
+        flce::bwd_band_kernel<T, false><<<grid, block, 0, s>>>(ga, da, g_long, g_grad, h_first);
+    }));
   }
   return FLCE_OK;
 }
@@ -299,7 +355,7 @@ int flce_plan(const flce_desc* d, flce_plan_info* out) {
   out->fwd_workgroups = p.Tv * int(cdiv(std::min<int64_t>(p.NF, std::max<int64_t>(p.N, 1)), 256));
   out->tile = flce::kTile;
   out->filter_block = kFilterBlock;
-  out->dz_bytes = int64_t(p.NS) * p.VS * p.es;
+  out->dz_bytes = int64_t(p.NS) * p.VS * p.es;   // one of the two dZ buffers
   return FLCE_OK;
 }
 

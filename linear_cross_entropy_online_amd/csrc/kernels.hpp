@@ -356,15 +356,43 @@ __device__ __forceinline__ void store4<float>(float* p, float a, float b, float 
   *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
 
+// Arguments of the dZ tiles of one band.
 template <typename T>
-__global__ void __launch_bounds__(kThreads, 1)
-bwd_dz_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* __restrict__ y,
-              const float* __restrict__ lse, const float* __restrict__ dloss_rows,
-              const Header* __restrict__ hdr, int N, int D, int V, int64_t ignore, int reduction,
-              float eps, BandArgs band, int TMv, int TNn, T* __restrict__ dz,
-              uint8_t* __restrict__ flags, uint8_t* __restrict__ flagsT) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
+struct DzArgs {
+  const T* H;
+  const T* W;
+  const int64_t* y;
+  const float* lse;
+  const float* dloss_rows;
+  const Header* hdr;
+  int N, D, V;
+  int64_t ignore;
+  int reduction;
+  float eps;
+  BandArgs band;
+  int TMv, TNn;          // vocabulary and token-row tiles of the band
+  T* dz;                 // the band's dZ buffer [ns][ldz]
+  uint8_t* flags;        // [frows][fcols]
+  uint8_t* flagsT;       // [fcols][frows]
+};
+
+// dZ tile t of a band: Z = W_v H_n^T recomputed, G = softmax(Z) - onehot(y),
+// dZ = g G (bf16 for bf16 inputs), plus the 64x64 filter flags.
+template <typename T>
+__device__ __forceinline__ void dz_tile(const DzArgs<T>& a, int t, char* lds) {
+  const T* __restrict__ H = a.H;
+  const T* __restrict__ W = a.W;
+  const int64_t* __restrict__ y = a.y;
+  const float* __restrict__ lse = a.lse;
+  const float* __restrict__ dloss_rows = a.dloss_rows;
+  const int N = a.N, D = a.D, V = a.V, reduction = a.reduction;
+  const int64_t ignore = a.ignore;
+  const float eps = a.eps;
+  const BandArgs& band = a.band;
+  const int TMv = a.TMv, TNn = a.TNn;
+  T* __restrict__ dz = a.dz;
+  uint8_t* __restrict__ flags = a.flags;
+  uint8_t* __restrict__ flagsT = a.flagsT;
   int tm, tn;
   grouped_tile(t, TMv, TNn, 4, tm, tn);
   const int v0 = band.vb0 + tm * kTile, n0 = band.nb0 + tn * kTile;
@@ -379,7 +407,7 @@ bwd_dz_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* _
   float g[4], ml[4];
   int rel[4];
   bool bad[4];
-  const float gs = hdr->gscale;
+  const float gs = a.hdr->gscale;
   const int vw = v0 + wm * 128;  // first vocabulary row of this wave's block
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -533,20 +561,35 @@ struct SkipRowsOfFlags {
 // row: the fp32 read-modify-write is one 16-byte access per 4 values.
 //   dH^T tile: A = W_band^T (stored [v][d]), B = dZ (stored [n][v]), K = v
 //   dW^T tile: A = H_band^T (stored [n][d]), B = dZ^T (stored [n][v]), K = n
+// Arguments of the gradient tiles of one band.
+template <typename T>
+struct GradArgs {
+  const T* H;
+  const T* W;
+  const T* dz;             // the band's dZ buffer
+  const uint8_t* flags;
+  const uint8_t* flagsT;
+  float* dH;
+  float* dW;
+  int N, D, V;
+  BandArgs band;
+  int T3n, T2n, Td;        // token-row tiles, vocabulary tiles, d tiles of the band
+  int beta_h, beta_w;      // accumulate into dH / dW (else overwrite)
+};
+
+// Gradient tile `local` of one of the band's two contractions (is_h: dH^T).
 template <typename T, bool FILTER>
-__global__ void __launch_bounds__(kThreads, 1)
-bwd_grad_kernel(const T* __restrict__ H, const T* __restrict__ W, const T* __restrict__ dz,
-                const uint8_t* __restrict__ flags, const uint8_t* __restrict__ flagsT,
-                float* __restrict__ dH, float* __restrict__ dW, int N, int D, int V,
-                BandArgs band, int T3n, int T2n, int Td, int beta_h, int beta_w) {
-  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
-  // The contraction with the longer K (dH^T: band vocabulary, dW^T: band
-  // rows) is dispatched first on every XCD.
-  const int T3 = Td * T3n, T2 = Td * T2n;
-  const bool h_first = band.vs_cur >= band.ns_cur;
-  const int t = xcd_remap_split(blockIdx.x, gridDim.x, h_first ? T3 : T2);
-  const bool is_h = h_first ? t < T3 : t >= T2;
-  const int local = h_first ? (is_h ? t : t - T3) : (is_h ? t - T2 : t);
+__device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int local, char* lds) {
+  const T* __restrict__ H = a.H;
+  const T* __restrict__ W = a.W;
+  const T* __restrict__ dz = a.dz;
+  const uint8_t* __restrict__ flags = a.flags;
+  const uint8_t* __restrict__ flagsT = a.flagsT;
+  float* __restrict__ dH = a.dH;
+  float* __restrict__ dW = a.dW;
+  const int D = a.D;
+  const BandArgs& band = a.band;
+  const int T3n = a.T3n, T2n = a.T2n, Td = a.Td, beta_h = a.beta_h, beta_w = a.beta_w;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   f32x16 acc[4][4];
@@ -619,8 +662,28 @@ bwd_grad_kernel(const T* __restrict__ H, const T* __restrict__ W, const T* __res
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off[i][q], 0, 0);
       }
   }
-  (void)N;
-  (void)V;
+}
+
+// One launch of the backward pipeline: the gradient tiles of band k - 1
+// (reading dZ buffer (k - 1) % 2) together with the dZ tiles of band k
+// (writing buffer k % 2), so that the tiles' memory-heavy epilogues do not
+// all fall at the same moment and no launch boundary sits between the two.
+// Tile kinds, longest first on every XCD: [0, g_long) gradient tiles of the
+// contraction with the longer K, [g_long, g_grad) the other gradient tiles,
+// [g_grad, G) dZ tiles.
+template <typename T, bool FILTER>
+__global__ void __launch_bounds__(kThreads, 1)
+bwd_band_kernel(GradArgs<T> ga, DzArgs<T> da, int g_long, int g_grad, int h_first) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  const int t = xcd_remap_kinds(blockIdx.x, gridDim.x, g_long, g_grad);
+  if (t >= g_grad) {
+    dz_tile<T>(da, t - g_grad, lds);
+    return;
+  }
+  const int T3 = ga.Td * ga.T3n;   // dH^T tiles
+  const bool is_h = h_first ? t < T3 : t >= g_long;
+  const int local = h_first ? (is_h ? t : t - T3) : (is_h ? t - g_long : t);
+  grad_tile<T, FILTER>(ga, is_h, local, lds);
 }
 
 }  // namespace flce

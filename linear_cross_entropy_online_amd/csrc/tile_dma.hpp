@@ -12,11 +12,15 @@
 //    128-byte lines (8 rows of a natural operand, 2 k rows of a transposed
 //    one): measured on MI355X, loads of half lines reach about half the
 //    L2-to-CU rate of whole lines.  Two stage slots of 64 KiB (A + B).
+//  * The LDS serves 256 bytes per clock (64 banks of 4 bytes; measured: 16
+//    lanes of a ds_read_b128 go in one clock), so each swizzle below spreads
+//    the lanes served together over all 64 banks.
 //  * Natural operands ([m][k], K contiguous) sit in LDS as [256 rows][128 B]:
-//    16-byte chunk c of row r at chunk c ^ (r & 7).  An MFMA fragment
+//    16-byte chunk c of row r at chunk c ^ ((r >> 1) & 7).  An MFMA fragment
 //    (8 K values of one row per lane) is one ds_read_b128.
 //  * Transposed operands ([k][m], M contiguous) sit in LDS as
-//    [64 k rows][512 B]: 32-byte segment s of row k at segment s ^ (k & 3).
+//    [64 k rows][512 B]: 32-byte segment s of row k at segment
+//    s ^ (2 (k & 3)).
 //    A fragment is two ds_read_b64_tr_b16: within each 16-lane group the
 //    hardware hands lane i the element (row kbase + e, column mbase + i),
 //    e = 0..3, when source lane j points at row kbase + j / 4, columns
@@ -96,10 +100,11 @@ __device__ __forceinline__ void barrier_raw() { asm volatile("s_barrier" ::: "me
 
 // natural [m][k]: instruction q of wave w covers tile rows 8 (8 w + q) .. +7
 // (128 bytes = 64 K values each); lane L -> row 8 (8 w + q) + L / 8, LDS
-// chunk L % 8, global chunk (L % 8) ^ (row % 8) = (L % 8) ^ (L / 8).
+// chunk L % 8, global chunk (L % 8) ^ ((row / 2) % 8), where
+// (row / 2) % 8 = 4 (q % 2) + L / 16.
 struct DmaNatural {
   uint32_t off[8];
-  int kc;                 // K element offset of this lane's chunk
+  int kc[2];              // K element offset of this lane's chunk, by q parity
   const char* base;       // element (m0, 0)
   int64_t ld, kext, mrem;
   __device__ __forceinline__ void init(const Operand& op, int m0, int wave, int lane) {
@@ -107,19 +112,21 @@ struct DmaNatural {
     ld = op.ld;
     kext = op.kext;
     mrem = op.mext - m0;
-    const int c = (lane & 7) ^ (lane >> 3);
-    kc = c * 8;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) kc[par] = ((lane & 7) ^ (4 * par + (lane >> 4))) * 8;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int row = 8 * (8 * wave + q) + (lane >> 3);
-      off[q] = (int64_t)m0 + row < op.mext ? (uint32_t)(((int64_t)row * op.ld + c * 8) * 2) : kOob;
+      off[q] = (int64_t)m0 + row < op.mext ? (uint32_t)(((int64_t)row * op.ld + kc[q & 1]) * 2)
+                                           : kOob;
     }
   }
   __device__ __forceinline__ void issue(uint32_t lds_op, int k0, int wave) const {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)k0 * 2);
-    const bool kin = k0 + kc < kext;
+    const bool kin0 = k0 + kc[0] < kext, kin1 = k0 + kc[1] < kext;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) dma16(lds_op + (8 * wave + q) * 1024, kin ? off[q] : kOob, rs);
+    for (int q = 0; q < 8; ++q)
+      dma16(lds_op + (8 * wave + q) * 1024, ((q & 1) ? kin1 : kin0) ? off[q] : kOob, rs);
   }
   // one 128-byte line per tile row: lane L touches row share * per + L % per
   __device__ __forceinline__ void prefetch(uint32_t lds_dummy, int k0, L2Split sp, int lane,
@@ -134,7 +141,8 @@ struct DmaNatural {
 
 // transposed [k][m]: instruction q of wave w covers k rows 2 (8 w + q), +1
 // (512 bytes = 256 M values each); lane L -> k row 2 (8 w + q) + L / 32, LDS
-// segment (L % 32) / 2, half L % 2, global segment ((L % 32) / 2) ^ (krow % 4).
+// segment (L % 32) / 2, half L % 2, global segment
+// ((L % 32) / 2) ^ (2 (krow % 4)).
 struct DmaTransposed {
   uint32_t off[8];
   bool colok[8];
@@ -150,7 +158,7 @@ struct DmaTransposed {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int krow = krow0 + 2 * q;
-      const int seg = ((lane & 31) >> 1) ^ (krow & 3);
+      const int seg = ((lane & 31) >> 1) ^ (2 * (krow & 3));
       const int m = seg * 16 + (lane & 1) * 8;
       colok[q] = (int64_t)m0 + m < op.mext;
       off[q] = (uint32_t)(((int64_t)krow * op.ld + m) * 2);
@@ -186,14 +194,14 @@ template <> struct DmaLoader<true> : DmaTransposed {};
 template <bool TRANS> struct FragReader;
 
 // natural: row r = wbase + 32 i + lane % 32, chunk 2 KS + lane / 32 stored at
-// chunk ^ (r % 8) = chunk ^ (lane % 8).
+// chunk ^ ((r / 2) % 8) = chunk ^ ((lane / 2) % 8).
 template <> struct FragReader<false> {
   int off[kDmaKs];   // per KS: byte offset of this lane's fragment in block i = 0
   __device__ __forceinline__ void init(int wbase, int lane) {
     const int r = wbase + (lane & 31);
 #pragma unroll
     for (int ks = 0; ks < kDmaKs; ++ks)
-      off[ks] = r * 128 + (((2 * ks + (lane >> 5)) ^ (lane & 7)) * 16);
+      off[ks] = r * 128 + (((2 * ks + (lane >> 5)) ^ ((lane >> 1) & 7)) * 16);
   }
   template <int KS>
   __device__ __forceinline__ void read(const char* s, bf16x8 (&f)[4]) const {
@@ -205,26 +213,25 @@ template <> struct FragReader<false> {
 
 // transposed: lane l of 16-lane group g4 = l / 16 (k half h = l / 32, column
 // half g = g4 % 2, j = l % 16) points at k row 16 KS + 8 h + 4 e + j / 4,
-// columns wbase + 32 i + 16 g + 4 (j % 4) .. +3 (segment swizzled by k % 4);
-// the transposing read hands it (k = 16 KS + 8 h + 4 e + 0..3, column
-// wbase + 32 i + l % 32).
+// columns wbase + 32 i + 16 g + 4 (j % 4) .. +3 (segment swizzled by
+// 2 (k % 4)); the transposing read hands it (k = 16 KS + 8 h + 4 e + 0..3,
+// column wbase + 32 i + l % 32).
 template <> struct FragReader<true> {
-  int addr[2];  // per (i & 1): byte address for KS 0, e 0
+  int addr[4];  // per block i: byte address for KS 0, e 0
   __device__ __forceinline__ void init(int wbase, int lane) {
     const int h = lane >> 5, g = (lane >> 4) & 1, j = lane & 15;
-    const int krow = 8 * h + (j >> 2);          // + 16 KS + 4 e
+    const int krow = 8 * h + (j >> 2);          // + 16 KS + 4 e (same k % 4)
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int seg = (wbase >> 4) + 2 * ii + g;  // 16 columns per 32-byte segment
-      addr[ii] = krow * 512 + ((seg ^ (krow & 3)) * 32) + (j & 3) * 8;
+    for (int i = 0; i < 4; ++i) {
+      const int seg = (wbase >> 4) + 2 * i + g;  // 16 columns per 32-byte segment
+      addr[i] = krow * 512 + ((seg ^ (2 * (krow & 3))) * 32) + (j & 3) * 8;
     }
   }
   template <int KS>
   __device__ __forceinline__ void read(const char* s, bf16x8 (&f)[4]) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // blocks i and i + 2 differ by 4 segments (128 bytes): an immediate
-      lds_char* p = (lds_char*)(s + addr[i & 1] + (i >> 1) * 128 + KS * 16 * 512);
+      lds_char* p = (lds_char*)(s + addr[i] + KS * 16 * 512);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
       f[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));

@@ -353,18 +353,29 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
   return x * q + (x < rem ? x : rem) + idx;
 }
 
-// As xcd_remap, for a grid whose tiles [0, T1) are longer than the rest:
-// XCD x gets an even share of each kind as two contiguous ranges and is sent
-// its long tiles first, so that no XCD is left holding most of the long work.
-__device__ __forceinline__ int xcd_remap_split(int b, int G, int T1) {
-  const int x = b & 7, idx = b >> 3;
-  const int q = G >> 3, rem = G & 7;
-  const int q1 = T1 >> 3, r1 = T1 & 7;
-  const int nl = q1 + (x < r1 ? 1 : 0);
-  const int l0 = x * q1 + (x < r1 ? x : r1);
-  if (idx < nl) return l0 + idx;
-  const int s0 = x * q + (x < rem ? x : rem) - l0;   // short tiles of the XCDs before x
-  return T1 + s0 + (idx - nl);
+// As xcd_remap, for a grid of three consecutive kinds of tiles [0, c1),
+// [c1, c2), [c2, G), longest first: XCD x gets an even share of every kind
+// as a contiguous range and is sent them kind by kind, so that no XCD is left
+// holding most of the long work.  The tiles of a kind that do not divide
+// evenly go one each to the XCDs that follow those given the previous
+// kind's, which keeps every XCD's total equal to the number of workgroups
+// the hardware sends it.
+__device__ __forceinline__ int xcd_remap_kinds(int b, int G, int c1, int c2) {
+  const int x = b & 7;
+  int idx = b >> 3, j0 = 0, lo = 0;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int hi = k == 0 ? c1 : (k == 1 ? c2 : G);
+    const int n = hi - lo, q = n >> 3, r = n & 7;
+    int before = 0;
+    for (int xx = 0; xx < x; ++xx) before += ((xx - j0) & 7) < r ? 1 : 0;
+    const int cnt = q + (((x - j0) & 7) < r ? 1 : 0);
+    if (idx < cnt) return lo + x * q + before + idx;
+    idx -= cnt;
+    j0 += r;
+    lo = hi;
+  }
+  return G;   // not reached for b < G
 }
 
 // Tile id t -> (tm, tn) in a TM x TN grid, visiting GM tile rows at a time.

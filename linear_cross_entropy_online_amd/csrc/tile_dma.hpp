@@ -128,6 +128,16 @@ struct DmaNatural {
     for (int q = 0; q < 8; ++q)
       dma16(lds_op + (8 * wave + q) * 1024, ((q & 1) ? kin1 : kin0) ? off[q] : kOob, rs);
   }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int k0) const {
+    return make_rsrc(base + (int64_t)k0 * 2);
+  }
+  // instruction Q alone (`more` false: every lane out of range, no memory access)
+  template <int Q>
+  __device__ __forceinline__ void issue_q(uint32_t lds_op, int k0, int wave, bool more,
+                                          __amdgpu_buffer_rsrc_t rs) const {
+    const bool kin = more && k0 + kc[Q & 1] < kext;
+    dma16(lds_op + (8 * wave + Q) * 1024, kin ? off[Q] : kOob, rs);
+  }
   // one 128-byte line per tile row: lane L touches row share * per + L % per
   __device__ __forceinline__ void prefetch(uint32_t lds_dummy, int k0, L2Split sp, int lane,
                                            bool on) const {
@@ -172,6 +182,15 @@ struct DmaTransposed {
       dma16(lds_op + (8 * wave + q) * 1024, ok ? off[q] : kOob, rs);
     }
   }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int k0) const {
+    return make_rsrc(base + (int64_t)k0 * ld * 2);
+  }
+  template <int Q>
+  __device__ __forceinline__ void issue_q(uint32_t lds_op, int k0, int wave, bool more,
+                                          __amdgpu_buffer_rsrc_t rs) const {
+    const bool ok = more && colok[Q] && (k0 + krow0 + 2 * Q < kext);
+    dma16(lds_op + (8 * wave + Q) * 1024, ok ? off[Q] : kOob, rs);
+  }
   // four 128-byte lines per k row: lane L touches line li = share * per + L % per,
   // k row li / 4, quarter li % 4
   __device__ __forceinline__ void prefetch(uint32_t lds_dummy, int k0, L2Split sp, int lane,
@@ -209,6 +228,10 @@ template <> struct FragReader<false> {
     for (int i = 0; i < 4; ++i)
       f[i] = *reinterpret_cast<const bf16x8*>(s + off[KS] + i * 32 * 128);
   }
+  template <int KS, int I>
+  __device__ __forceinline__ void read_blk(const char* s, bf16x8 (&f)[4]) const {
+    f[I] = *reinterpret_cast<const bf16x8*>(s + off[KS] + I * 32 * 128);
+  }
 };
 
 // transposed: lane l of 16-lane group g4 = l / 16 (k half h = l / 32, column
@@ -227,17 +250,36 @@ template <> struct FragReader<true> {
       addr[i] = krow * 512 + ((seg ^ (2 * (krow & 3))) * 32) + (j & 3) * 8;
     }
   }
+  template <int KS, int I>
+  __device__ __forceinline__ void read_blk(const char* s, bf16x8 (&f)[4]) const {
+    lds_char* p = (lds_char*)(s + addr[I] + KS * 16 * 512);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
+    f[I] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
   template <int KS>
   __device__ __forceinline__ void read(const char* s, bf16x8 (&f)[4]) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lds_char* p = (lds_char*)(s + addr[i] + KS * 16 * 512);
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
-      f[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
+    read_blk<KS, 0>(s, f);
+    read_blk<KS, 1>(s, f);
+    read_blk<KS, 2>(s, f);
+    read_blk<KS, 3>(s, f);
   }
 };
+
+// Fragments of sub-step KS of both operands, read in the order the MFMA
+// group uses them (A0 with B0..B3 first, then A1..A3).
+template <int KS, bool AT, bool BT>
+__device__ __forceinline__ void read_frags(const FragReader<AT>& fa, const FragReader<BT>& fb,
+                                           const char* s, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+  fa.template read_blk<KS, 0>(s, a);
+  fb.template read_blk<KS, 0>(s + kDmaOpBytes, b);
+  fb.template read_blk<KS, 1>(s + kDmaOpBytes, b);
+  fb.template read_blk<KS, 2>(s + kDmaOpBytes, b);
+  fb.template read_blk<KS, 3>(s + kDmaOpBytes, b);
+  fa.template read_blk<KS, 1>(s, a);
+  fa.template read_blk<KS, 2>(s, a);
+  fa.template read_blk<KS, 3>(s, a);
+}
 
 // Scheduling pattern for a 16-MFMA group that hides the R fragment reads of
 // the next group: 8 x {R/8 LDS reads, 2 MFMA} (R = 8, 12 or 16: one read per
@@ -262,6 +304,37 @@ __device__ __forceinline__ void mfma_group(f32x16 (&acc)[4][4], const bf16x8 (&a
     for (int j = 0; j < 4; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], FRESH ? zero : acc[i][j],
                                                           0, 0, 0);
+}
+
+// The last MFMA sub-step of a stage, right after the barrier that frees the
+// stage's slot: eight steps of {one DMA instruction of each operand for the
+// stage after next, one fragment read of the next stage's first sub-step (in
+// the order its MFMAs use them: A0, B0..B3, A1..A3), the two MFMAs of blocks
+// (P / 2, 2 (P % 2)) and (P / 2, 2 (P % 2) + 1)}, pinned in that order so
+// that a DMA instruction that has to wait for the address unit does not hold
+// back more than the MFMAs already issued.
+template <int P, bool AT, bool BT>
+__device__ __forceinline__ void last_substep(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
+                                             const bf16x8 (&b)[4], const DmaLoader<AT>& la,
+                                             const DmaLoader<BT>& lb, uint32_t la_op,
+                                             uint32_t lb_op, int k0, bool more, int wave,
+                                             __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb,
+                                             const FragReader<AT>& fa, const FragReader<BT>& fb,
+                                             const char* sn, bf16x8 (&an)[4], bf16x8 (&bn)[4]) {
+  if constexpr (P < 8) {
+    la.template issue_q<P>(la_op, k0, wave, more, rsa);
+    lb.template issue_q<P>(lb_op, k0, wave, more, rsb);
+    // A0, B0..B3, A1..A3: the order the next sub-step's MFMAs use them
+    if constexpr (P == 0) fa.template read_blk<0, 0>(sn, an);
+    else if constexpr (P <= 4) fb.template read_blk<0, P - 1>(sn + kDmaOpBytes, bn);
+    else fa.template read_blk<0, P - 4>(sn, an);
+    constexpr int i = P / 2, j = 2 * (P % 2);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    acc[i][j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j + 1], acc[i][j + 1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    last_substep<P + 1, AT, BT>(acc, a, b, la, lb, la_op, lb_op, k0, more, wave, rsa, rsb, fa, fb,
+                                sn, an, bn);
+  }
 }
 
 // acc = sum over active K steps (64 wide) of A[m][k] B[n][k] for the
@@ -333,10 +406,8 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand& A, const Operand& B
   }
   barrier_raw();
   bf16x8 a0[4], b0[4], a1[4], b1[4];
-  fa.template read<0>(lds, a0);
-  fb.template read<0>(lds + kDmaOpBytes, b0);
-  fa.template read<1>(lds, a1);
-  fb.template read<1>(lds + kDmaOpBytes, b1);
+  read_frags<0, AT, BT>(fa, fb, lds, a0, b0);
+  read_frags<1, AT, BT>(fa, fb, lds, a1, b1);
   mfma_group<true>(acc, a0, b0);
   interleave_reads_mfma<kReads>();
 
@@ -347,12 +418,10 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand& A, const Operand& B
   // conservative and stall on those reads).
   while (nxt < nsteps) {
     const char* s = lds + slot * kDmaStageBytes;
-    fa.template read<2>(s, a0);
-    fb.template read<2>(s + kDmaOpBytes, b0);
+    read_frags<2, AT, BT>(fa, fb, s, a0, b0);
     mfma_group<false>(acc, a1, b1);
     interleave_reads_mfma<kReads>();
-    fa.template read<3>(s, a1);
-    fb.template read<3>(s + kDmaOpBytes, b1);
+    read_frags<3, AT, BT>(fa, fb, s, a1, b1);
     mfma_group<false>(acc, a0, b0);
     interleave_reads_mfma<kReads>();
     const int nn = active.next(nxt + 1, nsteps);   // the stage after next
@@ -361,15 +430,20 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand& A, const Operand& B
     wait_vmcnt<1>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own reads of this slot
     barrier_raw();
-    if (nn < nsteps) issue(slot, nn);              // every wave is done with this slot
-    prefetch(nn + 2);
-    const char* sn = lds + (slot ^ 1) * kDmaStageBytes;
-    fa.template read<0>(sn, a0);
-    fb.template read<0>(sn + kDmaOpBytes, b0);
-    mfma_group<false>(acc, a1, b1);
-    interleave_reads_mfma<kReads>();
-    fa.template read<1>(sn, a1);
-    fb.template read<1>(sn + kDmaOpBytes, b1);
+    // every wave is done with this slot: it takes the stage after next
+    {
+      const bool more = nn < nsteps;
+      const int k0n = (more ? nn : 0) * kDmaKStep;
+      const uint32_t la_op = lbase + slot * kDmaStageBytes;
+      const char* sn = lds + (slot ^ 1) * kDmaStageBytes;
+      last_substep<0, AT, BT>(acc, a1, b1, la, lb, la_op, la_op + kDmaOpBytes, k0n, more, wave,
+                              la.rsrc(k0n), lb.rsrc(k0n), fa, fb, sn, a0, b0);
+    }
+    prefetch(nn + 2);   // after the DMAs: the wait above leaves only this one in flight
+    {
+      const char* sn = lds + (slot ^ 1) * kDmaStageBytes;
+      read_frags<1, AT, BT>(fa, fb, sn, a1, b1);
+    }
     mfma_group<false>(acc, a0, b0);
     interleave_reads_mfma<kReads>();
     nxt = nn;
@@ -377,15 +451,14 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand& A, const Operand& B
   }
   {
     const char* s = lds + slot * kDmaStageBytes;
-    fa.template read<2>(s, a0);
-    fb.template read<2>(s + kDmaOpBytes, b0);
+    read_frags<2, AT, BT>(fa, fb, s, a0, b0);
     mfma_group<false>(acc, a1, b1);
-    fa.template read<3>(s, a1);
-    fb.template read<3>(s + kDmaOpBytes, b1);
+    read_frags<3, AT, BT>(fa, fb, s, a1, b1);
     mfma_group<false>(acc, a0, b0);
     mfma_group<false>(acc, a1, b1);
   }
   acc_fence(acc);
+  wait_vmcnt<0>();   // DMAs past the last stage (out of range: zeros) and line touches
   __syncthreads();   // LDS may be reused by the caller
 }
 

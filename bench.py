@@ -25,6 +25,145 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
+SRC_DIR = os.path.join(ROOT, "linear_cross_entropy_online_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "bwd_band_8192x2048x151552_hbm_traffic.txt")
+DOMINANT = "bwd_band_kernel<unsigned short, false>"   # the backward launch of the default run
+
+
+def source_hash():
+    """sha256 over the kernel sources: a stored traffic figure holds only for
+    the kernels it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(SRC_DIR)):
+        if name.endswith((".hpp", ".hip")):
+            h.update(name.encode())
+            with open(os.path.join(SRC_DIR, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the dominant backward launch, from the committed
+    rocprofv3 --pmc summary, or None if absent or measured on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha256") != source_hash():
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def copy_calibration(nbytes):
+    """A plain device copy of known size (read nbytes, write nbytes) for
+    scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "dispatches": 3}), flush=True)
+
+
+def _pmc_rows(d):
+    import csv
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(root, fn)) as f:
+                    yield from csv.DictReader(f)
+
+
+def _pmc_kib(d, counter, match):
+    """Per-dispatch value of `counter` (KiB) for kernels whose name contains every
+    string of `match`; summed over the counter's rows of one dispatch."""
+    per = {}
+    for r in _pmc_rows(d):
+        if r["Counter_Name"] == counter and all(m in r["Kernel_Name"] for m in match):
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return sorted(per.values())
+
+
+def summarize_pmc(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_bytes, out, cmds):
+    import statistics
+    copy = ("elementwise", "Mul")
+    cf = statistics.median(_pmc_kib(cal_fetch_dir, "FETCH_SIZE", copy))
+    cw = statistics.median(_pmc_kib(cal_write_dir, "WRITE_SIZE", copy))
+    kib = cal_bytes / 1024.0
+    ff, fw = kib / cf, kib / cw
+    f = _pmc_kib(fetch_dir, "FETCH_SIZE", (DOMINANT,))
+    w = _pmc_kib(write_dir, "WRITE_SIZE", (DOMINANT,))
+    fm, wm = statistics.median(f), statistics.median(w)
+    hbm = (fm * ff + wm * fw) * 1024.0
+    lines = ["# HBM traffic of the backward band launch (bwd_band_kernel, bf16, filter off),",
+             "# 8192 x 2048 x 151552 bf16, mean, 5% ignored; rocprofv3 --pmc, one counter per run.",
+             "# Counters scaled by what they read for a plain copy of known size (torch.mul by 1",
+             "# of a float tensor: reads and writes exactly the tensor).",
+             "# Commands (run from the repository root on one MI355X):"]
+    lines += [f"#   {c}" for c in cmds]
+    lines += [f"kernel: flce::{DOMINANT}",
+              f"dispatches_measured: {len(f)} (FETCH_SIZE), {len(w)} (WRITE_SIZE)",
+              f"fetch_kib_per_launch_median: {fm:.1f}",
+              f"write_kib_per_launch_median: {wm:.1f}",
+              f"copy_bytes: {cal_bytes}",
+              f"copy_fetch_kib: {cf:.1f}",
+              f"copy_write_kib: {cw:.1f}",
+              f"fetch_scale: {ff:.4f}",
+              f"write_scale: {fw:.4f}",
+              f"hbm_bytes_per_launch: {hbm:.0f}",
+              f"source_sha256: {source_hash()}"]
+    with open(out, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_trace(d, out, title, cmd, bench_json=None):
+    import csv
+    stats = trace = None
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith("kernel_stats.csv"):
+                stats = os.path.join(root, fn)
+            elif fn.endswith("kernel_trace.csv"):
+                trace = os.path.join(root, fn)
+    rows = list(csv.DictReader(open(stats)))
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```", cmd,
+             "```", "", "Per-kernel statistics (rocprofv3 `--kernel-trace --stats`):", "",
+             "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].split("(")[0].replace("void ", "")
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    if trace:
+        seen = {}
+        for t in csv.DictReader(open(trace)):
+            name = t["Kernel_Name"].split("(")[0].replace("void ", "")
+            if name not in seen:
+                seen[name] = [t.get(k, "") for k in ("LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+                                                     "Accum_VGPR_Count", "SGPR_Count",
+                                                     "Workgroup_Size_X", "Grid_Size_X")]
+        lines += ["", "Launch resources (first dispatch of each kernel):", "",
+                  "| kernel | LDS B | scratch B/lane | VGPR | AGPR | SGPR | block | grid (threads) |",
+                  "|---|---|---|---|---|---|---|---|"]
+        for k, v in seen.items():
+            lines.append(f"| `{k}` | " + " | ".join(v) + " |")
+    if bench_json:
+        b = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        keep = {k: b[k] for k in ("value", "ms_per_step", "mfma_util", "roofline", "peak_extra_mib")}
+        lines += ["", "Same build, `bench.py` line (default arguments, separate run):", "", "```",
+                  json.dumps(keep), "```"]
+    with open(out, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -32,9 +171,20 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="large_vocab")
     p.add_argument("--filter-eps", type=float, default=0.0)
-    p.add_argument("--cpu-rows", type=int, default=1024,
+    p.add_argument("--cpu-rows", type=int, default=8192,
                    help="rows of the workload the oracle runs for cpu_baseline (0 = skip)")
     p.add_argument("--no-profile-pass", action="store_true")
+    # measurement helpers (no bench line): see profiles/ for the commands that use them
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="run a plain device copy of BYTES (for scaling FETCH_SIZE / WRITE_SIZE)")
+    p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR",
+                                                         "CAL_WRITE_DIR"))
+    p.add_argument("--summarize-trace", metavar="DIR")
+    p.add_argument("--cal-bytes", type=int, default=1 << 30)
+    p.add_argument("--out")
+    p.add_argument("--title", default="")
+    p.add_argument("--cmd", action="append", default=[])
+    p.add_argument("--bench-json")
     return p.parse_args()
 
 
@@ -81,6 +231,16 @@ def cpu_baseline(H, W, y, reduction, rows):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.cal_bytes, args.out, args.cmd)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, args.title, " ".join(args.cmd),
+                        args.bench_json)
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path's sharding is described in DESIGN.md)", file=sys.stderr)
@@ -157,9 +317,12 @@ def main():
         launches = kernels[dom]["launches_per_step"]
         per_launch = flops_per_step[dom] / launches
         achieved = per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+        traffic = None
+        if dom == "bwd_band" and args.workload == "large_vocab" and args.filter_eps == 0.0:
+            traffic = stored_traffic()
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                     "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                    "traffic": None, "flops_per_launch": per_launch,
+                    "traffic": traffic, "flops_per_launch": per_launch,
                     "avg_launch_ms": kernels[dom]["avg_ms"]}
 
     cpu = None

@@ -136,6 +136,20 @@ int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const i
                        float* dH, float* dW,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Multiplies dH [N,D] and dW [V,D] (float, in place, 16-byte aligned) by the
+ * upstream gradient dloss[0] (device pointer; NULL means 1: nothing to do).
+ * Together with flce_fused_fwd_bwd this is the contract in which the forward
+ * already computes the gradients: p1 (Trillion Labs FLCE notes) section
+ * "6. Backward는 새 logits를 만들지 않음" and p2 (PyTorch 2.13
+ * LinearCrossEntropyLoss chapter) section "scalar reduction에서는 forward가
+ * gradient까지 계산한다": for mean and sum the forward produces dH and dW with
+ * an upstream gradient of 1 and the backward only scales them by the upstream
+ * scalar.  reduction == FLCE_NONE returns FLCE_E_UNSUPPORTED: a per-row
+ * upstream gradient cannot be applied after the contraction, so that path
+ * recomputes (flce_backward).  No workspace is used. */
+int flce_scale_gradients(const flce_desc* d, const float* dloss, float* dH, float* dW,
+                         hipStream_t stream);
+
 /* Synchronises `stream`, then reads the status word of `ws` into *out
  * (bit 0: a target outside [0, V) that is not ignore_index). */
 int flce_device_status(const void* ws, hipStream_t stream, int32_t* out);

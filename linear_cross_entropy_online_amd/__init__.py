@@ -27,7 +27,7 @@ from ._abi import (FLCE_BF16, FLCE_F32, FLCE_FLAG_PROFILE, FLCE_K_AUX, FLCE_K_BW
                    FLCE_K_LSE_COMBINE, FLCE_MEAN, FLCE_NONE, FLCE_SUM, FlceError, lib)
 
 __all__ = ["flce_workspace_bytes", "flce_plan", "flce_forward", "flce_backward",
-           "flce_fused_fwd_bwd", "flce_device_status", "flce_profile_reset",
+           "flce_fused_fwd_bwd", "flce_scale_gradients", "flce_device_status", "flce_profile_reset",
            "flce_profile_read", "linear_cross_entropy", "Workspace", "FlceError", "lib",
            "FLCE_FLAG_PROFILE", "KERNEL_CLASSES"]
 
@@ -187,6 +187,21 @@ def flce_fused_fwd_bwd(H, W, y, reduction="mean", ignore_index=-100, filter_eps=
     return loss, loss_rows, lse, dH, dW
 
 
+def flce_scale_gradients(dH, dW, dloss, reduction="mean", dtype=torch.bfloat16):
+    """dH *= dloss[0], dW *= dloss[0] in place on the device (dloss: device float32
+    [1], or None for 1).  reduction "none" is rejected by the library."""
+    N, D = dH.shape
+    V = dW.shape[0]
+    d = make_desc(N, D, V, dtype, reduction)
+    if dloss is not None:
+        dloss = dloss.to(device=dW.device, dtype=torch.float32).reshape(-1).contiguous()
+        if dloss.numel() != 1:
+            raise FlceError(_abi.FLCE_E_SHAPE, "dloss must have 1 element")
+    _abi.check(lib().flce_scale_gradients(ctypes.byref(d), _ptr(dloss), _ptr(dH), _ptr(dW),
+                                          _stream(dW.device)))
+    return dH, dW
+
+
 def flce_device_status(ws: Workspace, device=None) -> int:
     out = ctypes.c_int32(0)
     dev = ws.buf.device if device is None else device
@@ -223,7 +238,42 @@ class _LinearCrossEntropy(torch.autograd.Function):
         return dH.to(H.dtype), dW.to(W.dtype), None, None, None, None
 
 
-def linear_cross_entropy(H, W, y, reduction="mean", ignore_index=-100, filter_eps=0.0):
-    """loss = CE(H W^T, y) without materialising the logits (autograd-aware)."""
+class _LinearCrossEntropyGradsInForward(torch.autograd.Function):
+    """mean / sum: the forward computes loss, dH and dW together (upstream
+    gradient 1) and keeps the gradients; the backward only scales them by the
+    upstream scalar (p1 section "6. Backward는 새 logits를 만들지 않음"; p2
+    section "scalar reduction에서는 forward가 gradient까지 계산한다").  The
+    kept gradients are consumed by the first backward: a second one raises."""
+    @staticmethod
+    def forward(ctx, H, W, y, reduction, ignore_index, filter_eps):
+        loss, _, _, dH, dW = flce_fused_fwd_bwd(H, W, y, reduction, ignore_index, filter_eps)
+        ctx.grads = (dH, dW)
+        ctx.dtypes = (H.dtype, W.dtype, reduction)
+        return loss.reshape(())
+
+    @staticmethod
+    def backward(ctx, g):
+        if ctx.grads is None:
+            raise RuntimeError("linear_cross_entropy(grads_in_forward=True): the gradients "
+                               "computed in the forward were already used by a backward")
+        dH, dW = ctx.grads
+        ctx.grads = None
+        h_dtype, w_dtype, reduction = ctx.dtypes
+        flce_scale_gradients(dH, dW, g.reshape(1).float(), reduction, h_dtype)
+        return dH.to(h_dtype), dW.to(w_dtype), None, None, None, None
+
+
+def linear_cross_entropy(H, W, y, reduction="mean", ignore_index=-100, filter_eps=0.0,
+                         grads_in_forward=False):
+    """loss = CE(H W^T, y) without materialising the logits (autograd-aware).
+
+    grads_in_forward: for mean / sum, do all the contraction work (forward,
+    recompute and gradients) inside the forward and only scale dH and dW by the
+    upstream scalar in the backward; dH and dW (fp32) are held from forward to
+    backward, and only one backward is allowed.  reduction "none" always
+    recomputes in the backward."""
+    if grads_in_forward and reduction != "none":
+        return _LinearCrossEntropyGradsInForward.apply(H, W, y, reduction, ignore_index,
+                                                       filter_eps)
     return _LinearCrossEntropy.apply(H, W, y, reduction, ignore_index, filter_eps)
 

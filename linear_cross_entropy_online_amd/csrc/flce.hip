@@ -434,6 +434,25 @@ int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const i
   return run_bands<float>(d, p, H, W, y, lse, nullptr, dH, dW, w, prof, stream);
 }
 
+int flce_scale_gradients(const flce_desc* d, const float* dloss, float* dH, float* dW,
+                         hipStream_t stream) {
+  Plan p;
+  FLCE_TRY(make_plan(d, p));
+  if (d->reduction == FLCE_NONE) return FLCE_E_UNSUPPORTED;
+  if (!dW || (p.N > 0 && !dH)) return FLCE_E_NULL;
+  if (!aligned(dW, 16) || (dH && !aligned(dH, 16)) || (dloss && !aligned(dloss, 4)))
+    return FLCE_E_ALIGN;
+  if (!dloss) return FLCE_OK;   // an upstream gradient of 1
+  const bool prof = d->flags & FLCE_FLAG_PROFILE;
+  if (p.N > 0)
+    FLCE_TRY(launch(FLCE_K_AUX, prof, stream, [&] {
+      flce::scale_f32_kernel<<<dim3(2048), dim3(256), 0, stream>>>(dH, p.N * p.D, dloss);
+    }));
+  return launch(FLCE_K_AUX, prof, stream, [&] {
+    flce::scale_f32_kernel<<<dim3(2048), dim3(256), 0, stream>>>(dW, p.V * p.D, dloss);
+  });
+}
+
 int flce_device_status(const void* ws, hipStream_t stream, int32_t* out) {
   if (!ws || !out) return FLCE_E_NULL;
   if (hipStreamSynchronize(stream) != hipSuccess) return FLCE_E_DEVICE;

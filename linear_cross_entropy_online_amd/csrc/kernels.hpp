@@ -329,6 +329,19 @@ __global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
 }
 
+// p[i] *= s[0] over n floats (p 16-byte aligned): the upstream scalar applied
+// to gradients computed with an upstream gradient of 1.
+__global__ void scale_f32_kernel(float* __restrict__ p, int64_t n, const float* __restrict__ s) {
+  const float g = s[0];
+  const int64_t n4 = n >> 2;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  f32x4* __restrict__ p4 = reinterpret_cast<f32x4*>(p);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    p4[i] = p4[i] * g;
+  for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    p[i] *= g;
+}
+
 __global__ void clear_status_kernel(Header* __restrict__ hdr, float* __restrict__ loss) {
   if (threadIdx.x == 0) {
     hdr->status = 0;

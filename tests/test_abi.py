@@ -104,6 +104,14 @@ def test_argument_errors_return_before_any_device_work():
                              _fake(A), need, None) == _abi.FLCE_E_NULL
     assert lib.flce_backward(ctypes.byref(d), ok[0], ok[1], ok[2], ok[3], None, _fake(A + 4),
                              ok[5], _fake(A), need, None) == _abi.FLCE_E_ALIGN
+    # scale_gradients: reduction none, NULL dW, misaligned dH; NULL dloss = nothing to do
+    dn = L.make_desc(8, 64, 10, reduction=_abi.FLCE_NONE)
+    assert lib.flce_scale_gradients(ctypes.byref(dn), ok[0], ok[1], ok[2], None) == \
+        _abi.FLCE_E_UNSUPPORTED
+    assert lib.flce_scale_gradients(ctypes.byref(d), ok[0], ok[1], None, None) == _abi.FLCE_E_NULL
+    assert lib.flce_scale_gradients(ctypes.byref(d), ok[0], _fake(A + 8), ok[2], None) == \
+        _abi.FLCE_E_ALIGN
+    assert lib.flce_scale_gradients(ctypes.byref(d), None, ok[1], ok[2], None) == _abi.FLCE_OK
     # fused: NULL workspace
     assert lib.flce_fused_fwd_bwd(ctypes.byref(d), *ok[:3], ok[3], ok[4], ok[5], ok[0], ok[1],
                                   None, need, None) == _abi.FLCE_E_NULL

@@ -221,6 +221,55 @@ def test_autograd_function():
     assert max_abs_rel(Wd.grad, ref["dW"]) < 5e-5
 
 
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_grads_in_forward_contract(reduction):
+    """Forward computes dH, dW; backward only scales by the upstream scalar
+    (fp32 inputs so the tolerance is the tight one)."""
+    H, W, y = fi.random_case(520, 72, 1300, seed=33, dtype="f32", sigma_w=0.08)
+    Hd = H.to(DEV).requires_grad_(True)
+    Wd = W.to(DEV).requires_grad_(True)
+    loss = L.linear_cross_entropy(Hd, Wd, y.to(DEV), reduction=reduction, grads_in_forward=True)
+    g = -0.37
+    (g * loss).backward(retain_graph=True)
+    ref = O.linear_cross_entropy(H, W, y, reduction=reduction, dloss=g)
+    report(f"grads_in_forward_{reduction}", loss=rel(loss.item(), ref["loss"]),
+           dH=max_abs_rel(Hd.grad, ref["dH"]), dW=max_abs_rel(Wd.grad, ref["dW"]))
+    assert rel(loss.item(), ref["loss"]) < TOL["f32"]["loss"]
+    assert max_abs_rel(Hd.grad, ref["dH"]) < TOL["f32"]["grad"]
+    assert max_abs_rel(Wd.grad, ref["dW"]) < TOL["f32"]["grad"]
+    with pytest.raises(RuntimeError):          # the kept gradients were consumed
+        loss.backward()
+
+
+def test_grads_in_forward_none_recomputes():
+    """reduction none has no scalar to apply afterwards: the flag falls back
+    to the recomputing backward, with per-row upstream gradients."""
+    H, W, y = fi.random_case(300, 64, 900, seed=34, dtype="f32", sigma_w=0.08)
+    Hd = H.to(DEV).requires_grad_(True)
+    Wd = W.to(DEV).requires_grad_(True)
+    rows = L.linear_cross_entropy(Hd, Wd, y.to(DEV), reduction="none", grads_in_forward=True)
+    gr = torch.randn(300, generator=torch.Generator().manual_seed(8), dtype=torch.float64)
+    (rows * gr.float().to(DEV)).sum().backward()
+    ref = O.linear_cross_entropy(H, W, y, reduction="none", dloss=gr.numpy())
+    assert max_abs_rel(rows, ref["loss_rows"]) < TOL["f32"]["loss"]
+    assert max_abs_rel(Hd.grad, ref["dH"]) < TOL["f32"]["grad"]
+    assert max_abs_rel(Wd.grad, ref["dW"]) < TOL["f32"]["grad"]
+
+
+def test_scale_gradients_is_an_exact_multiply():
+    """The scale kernel is one fp32 multiply per element: bitwise equal to
+    torch's (row counts that are not multiples of the kernel's grid)."""
+    gen = torch.Generator().manual_seed(9)
+    dH = torch.randn(37, 24, generator=gen).to(DEV)
+    dW = torch.randn(101, 24, generator=gen).to(DEV)
+    g = torch.tensor([0.123456789], device=DEV)
+    eH, eW = dH * g, dW * g
+    L.flce_scale_gradients(dH, dW, g, "sum")
+    assert torch.equal(dH, eH) and torch.equal(dW, eW)
+    with pytest.raises(L.FlceError):
+        L.flce_scale_gradients(dH, dW, g, "none")
+
+
 def test_vocab_permutation():
     H, W, y = fi.random_case(300, 64, 1200, seed=31)
     perm = torch.randperm(1200, generator=torch.Generator().manual_seed(1))

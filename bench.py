@@ -306,6 +306,20 @@ def main():
                                  "ms_per_step": t / args.steps}
         print(f"bench: kernels {json.dumps(kernels)}", file=sys.stderr, flush=True)
 
+    # the "forward computes gradients" contract adds one kernel to a step: the
+    # backward's scaling of dH and dW by the upstream scalar (fp32, in place)
+    scale_ms = None
+    if wl.reduction != "none":
+        g1 = torch.ones(1, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        L.flce_scale_gradients(outs[3], outs[4], g1, wl.reduction, Hd.dtype)
+        e0.record()
+        for _ in range(5):
+            L.flce_scale_gradients(outs[3], outs[4], g1, wl.reduction, Hd.dtype)
+        e1.record()
+        torch.cuda.synchronize()
+        scale_ms = e0.elapsed_time(e1) / 5
+
     # algorithmic flops per step of each contraction class, for this plan
     NS, VS = plan["band_rows"], plan["band_vocab"]
     n_bands = plan["n_bands_rows"] * plan["n_bands_vocab"]
@@ -347,6 +361,7 @@ def main():
         "plan": {"band_rows": NS, "band_vocab": VS, "bands": n_bands,
                  "fwd_band_rows": plan["fwd_band_rows"], "fwd_workgroups": plan["fwd_workgroups"]},
         "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
+        "grads_in_forward_scale_ms": None if scale_ms is None else round(scale_ms, 4),
     }
     print(json.dumps(line), flush=True)
 

@@ -499,21 +499,45 @@ __device__ __forceinline__ void dz_tile(const DzArgs<T>& a, int t, char* lds) {
         flagsT[fc * band.frows + fr] = kp ? 0 : 1;
       }
     }
-    // dZ = g (p - onehot) into the band [rows of the band][vocab], row stride ldz
+    // dZ = g (p - onehot).  bf16: into the LDS copy of the tile ([256 token
+    // rows][512 B], 16-byte chunk c of row r at chunk c ^ (r % 32), so the 32
+    // rows one instruction writes spread over all banks), stored to the band
+    // below in whole rows.  fp32: straight to the band.
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
-      const int nl = n0 - band.nb0 + wn * 128 + (2 * bj + jj) * 32 + (lane & 31);
-      T* row = dz + (int64_t)nl * band.ldz + (vw - band.vb0);
+      const int r = wn * 128 + (2 * bj + jj) * 32 + (lane & 31);   // tile row
+      T* row = dz + (int64_t)(n0 - band.nb0 + r) * band.ldz + (vw - band.vb0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float gg = gk[i >> 1][jj];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int c = i * 32 + 8 * q + 4 * (lane >> 5);
-          store4<T>(row + c, gg * p[jj][i][4 * q + 0], gg * p[jj][i][4 * q + 1],
-                    gg * p[jj][i][4 * q + 2], gg * p[jj][i][4 * q + 3]);
+          const int c = i * 32 + 8 * q + 4 * (lane >> 5);        // column within the wave's 128
+          if constexpr (sizeof(T) == 2) {
+            const int col = wm * 128 + c;                          // tile column
+            *reinterpret_cast<u32x2*>(lds + r * 512 + (((col >> 3) ^ (r & 31)) * 16) +
+                                      ((col >> 2) & 1) * 8) =
+                u32x2{pack_bf16x2(gg * p[jj][i][4 * q + 0], gg * p[jj][i][4 * q + 1]),
+                      pack_bf16x2(gg * p[jj][i][4 * q + 2], gg * p[jj][i][4 * q + 3])};
+          } else {
+            store4<T>(row + c, gg * p[jj][i][4 * q + 0], gg * p[jj][i][4 * q + 1],
+                      gg * p[jj][i][4 * q + 2], gg * p[jj][i][4 * q + 3]);
+          }
         }
       }
+    }
+  }
+  if constexpr (sizeof(T) == 2) {
+    // The tile's 128 KiB of bf16 dZ from LDS to the band: wave w stores rows
+    // 64 w .. 64 w + 63, two whole 512-byte rows per instruction.
+    __syncthreads();
+    const int half = lane >> 5, ch = lane & 31;
+    T* base = dz + (int64_t)(n0 - band.nb0) * band.ldz + (v0 - band.vb0);
+#pragma unroll 8
+    for (int s2 = 0; s2 < 32; ++s2) {
+      const int r = 64 * wave + 2 * s2 + half;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * 512 + ((ch ^ (r & 31)) * 16));
+      *reinterpret_cast<u32x4*>(base + (int64_t)r * band.ldz + ch * 8) = v;
     }
   }
 }

@@ -171,6 +171,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="large_vocab")
     p.add_argument("--filter-eps", type=float, default=0.0)
+    p.add_argument("--compact-ignored", action="store_true",
+                   help="remove rows whose target is ignore_index before every contraction")
     p.add_argument("--cpu-rows", type=int, default=8192,
                    help="rows of the workload the oracle runs for cpu_baseline (0 = skip)")
     p.add_argument("--no-profile-pass", action="store_true")
@@ -195,7 +197,8 @@ def backward_flops_by_class(plan, N, D, V):
     launch is class bwd_dz, the last bwd_grad, the others bwd_band."""
     NS, VS, nbn, nbv = (plan["band_rows"], plan["band_vocab"], plan["n_bands_rows"],
                         plan["n_bands_vocab"])
-    bands = [(min(NS, N - bn * NS), min(VS, V - bv * VS)) for bn in range(nbn) for bv in range(nbv)]
+    bands = [(max(0, min(NS, N - bn * NS)), min(VS, V - bv * VS)) for bn in range(nbn)
+             for bv in range(nbv)]
     out = {"bwd_dz": 0.0, "bwd_grad": 0.0, "bwd_band": 0.0}
     nb = len(bands)
     for k in range(nb + 1):
@@ -258,15 +261,16 @@ def main():
     H, W, y = fi.make(wl.name)
     Hd, Wd, yd = H.to(dev), W.to(dev), y.to(dev)
     N, D, V = wl.n, wl.d, wl.v
+    flags0 = L.FLCE_FLAG_COMPACT_IGNORED if args.compact_ignored else 0
     plan = L.flce_plan(N, D, V, dtype=Hd.dtype, reduction=wl.reduction,
-                       filter_eps=args.filter_eps)
+                       filter_eps=args.filter_eps, flags=flags0)
     ws = L.Workspace(plan["ws_bytes"], dev)
     outs = (torch.empty(1, device=dev), torch.empty(N, device=dev), torch.empty(N, device=dev),
             torch.empty(N, D, device=dev), torch.empty(V, D, device=dev))
 
     def step(flags=0):
         L.flce_fused_fwd_bwd(Hd, Wd, yd, reduction=wl.reduction, filter_eps=args.filter_eps,
-                             flags=flags, ws=ws, out=outs)
+                             flags=flags | flags0, ws=ws, out=outs)
 
     for _ in range(args.warmup):
         step()
@@ -323,8 +327,10 @@ def main():
     # algorithmic flops per step of each contraction class, for this plan
     NS, VS = plan["band_rows"], plan["band_vocab"]
     n_bands = plan["n_bands_rows"] * plan["n_bands_vocab"]
-    flops_per_step = backward_flops_by_class(plan, N, D, V)
-    flops_per_step["fwd_lse"] = 2.0 * ndv
+    # with compaction the contractions cover only the kept rows
+    n_eff = int((y != fi.IGNORE_INDEX).sum()) if args.compact_ignored else N
+    flops_per_step = backward_flops_by_class(plan, n_eff, D, V)
+    flops_per_step["fwd_lse"] = 2.0 * n_eff * D * V
     roofline = None
     if kernels:
         dom = max((k for k in kernels if k in flops_per_step), key=lambda k: kernels[k]["ms_per_step"])
@@ -332,7 +338,8 @@ def main():
         per_launch = flops_per_step[dom] / launches
         achieved = per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
         traffic = None
-        if dom == "bwd_band" and args.workload == "large_vocab" and args.filter_eps == 0.0:
+        if (dom == "bwd_band" and args.workload == "large_vocab" and args.filter_eps == 0.0
+                and not args.compact_ignored):
             traffic = stored_traffic()
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                     "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -351,6 +358,7 @@ def main():
         "dtype": wl.dtype, "data": "synthetic (seeded N(0,1) H, N(0,0.02^2) W, uniform targets)",
         "config": {"workload": wl.name, "N": N, "D": D, "V": V, "reduction": wl.reduction,
                    "ignore_frac": wl.ignore_frac, "filter_eps": args.filter_eps,
+                   "compact_ignored": bool(args.compact_ignored),
                    "parallelism": "single GPU"},
         "mfma_util": round(tflops / peak, 4), "tflops_counted_8ndv": round(tflops, 1),
         "ms_median": round(float(np.median(per)), 4), "ms_p95": round(float(np.percentile(per, 95)), 4),

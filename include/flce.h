@@ -68,8 +68,19 @@ enum { FLCE_BF16 = 0, FLCE_F32 = 1 };             /* element type of H and W   *
 enum { FLCE_MEAN = 0, FLCE_SUM = 1, FLCE_NONE = 2 }; /* loss reduction           */
 
 /* Bits of flce_desc.flags. */
-enum { FLCE_FLAG_PROFILE = 1u };   /* record HIP events around every launch (see
+enum {
+  FLCE_FLAG_PROFILE = 1u,          /* record HIP events around every launch (see
                                       flce_profile_read); costs a little time  */
+  FLCE_FLAG_COMPACT_IGNORED = 2u   /* remove the rows whose target is ignore_index
+                                      before every contraction (CCE App. B):
+                                      the tiles cover only the other rows.  Their
+                                      loss_rows entry, dH row and dW contribution
+                                      are 0 as without the flag, but their lse
+                                      entry is 0 (not computed).  bf16 inputs
+                                      only, and N * D * 4 < 2^31; otherwise
+                                      FLCE_E_UNSUPPORTED.  Adds N int32 and
+                                      ceil(N/1024) int32 to the workspace.    */
+};
 
 typedef struct flce_desc {
   int64_t n_rows;          /* N >= 0 token rows                                */

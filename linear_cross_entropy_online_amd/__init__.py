@@ -22,14 +22,15 @@ import ctypes
 import torch
 
 from . import _abi
-from ._abi import (FLCE_BF16, FLCE_F32, FLCE_FLAG_PROFILE, FLCE_K_AUX, FLCE_K_BWD_BAND,
+from ._abi import (FLCE_BF16, FLCE_F32, FLCE_FLAG_COMPACT_IGNORED, FLCE_FLAG_PROFILE, FLCE_K_AUX,
+                   FLCE_K_BWD_BAND,
                    FLCE_K_BWD_DZ, FLCE_K_BWD_GRAD, FLCE_K_COUNT, FLCE_K_FINALIZE, FLCE_K_FWD_LSE,
                    FLCE_K_LSE_COMBINE, FLCE_MEAN, FLCE_NONE, FLCE_SUM, FlceError, lib)
 
 __all__ = ["flce_workspace_bytes", "flce_plan", "flce_forward", "flce_backward",
            "flce_fused_fwd_bwd", "flce_scale_gradients", "flce_device_status", "flce_profile_reset",
            "flce_profile_read", "linear_cross_entropy", "Workspace", "FlceError", "lib",
-           "FLCE_FLAG_PROFILE", "KERNEL_CLASSES"]
+           "FLCE_FLAG_PROFILE", "FLCE_FLAG_COMPACT_IGNORED", "KERNEL_CLASSES"]
 
 _RED = {"mean": FLCE_MEAN, "sum": FLCE_SUM, "none": FLCE_NONE}
 KERNEL_CLASSES = {"fwd_lse": FLCE_K_FWD_LSE, "lse_combine": FLCE_K_LSE_COMBINE,
@@ -66,8 +67,8 @@ def flce_workspace_bytes(N, D, V, dtype=torch.bfloat16, reduction="mean", ignore
 
 
 def flce_plan(N, D, V, dtype=torch.bfloat16, reduction="mean", ignore_index=-100,
-              filter_eps=0.0, ws_budget_bytes=0) -> dict:
-    d = make_desc(N, D, V, dtype, reduction, ignore_index, filter_eps, 0, ws_budget_bytes)
+              filter_eps=0.0, ws_budget_bytes=0, flags=0) -> dict:
+    d = make_desc(N, D, V, dtype, reduction, ignore_index, filter_eps, flags, ws_budget_bytes)
     info = _abi.FlcePlanInfo()
     _abi.check(lib().flce_plan(ctypes.byref(d), ctypes.byref(info)))
     return {k: getattr(info, k) for k, _ in _abi.FlcePlanInfo._fields_}

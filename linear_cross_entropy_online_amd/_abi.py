@@ -12,6 +12,7 @@ FLCE_E_WORKSPACE, FLCE_E_UNSUPPORTED, FLCE_E_LAUNCH, FLCE_E_DEVICE = 5, 6, 7, 8
 FLCE_BF16, FLCE_F32 = 0, 1
 FLCE_MEAN, FLCE_SUM, FLCE_NONE = 0, 1, 2
 FLCE_FLAG_PROFILE = 1
+FLCE_FLAG_COMPACT_IGNORED = 2
 (FLCE_K_FWD_LSE, FLCE_K_LSE_COMBINE, FLCE_K_FINALIZE, FLCE_K_BWD_DZ, FLCE_K_BWD_GRAD,
  FLCE_K_AUX, FLCE_K_BWD_BAND, FLCE_K_COUNT) = range(8)
 

@@ -48,6 +48,9 @@ struct Plan {
   size_t big;          // bytes shared by the forward partials and the dZ buffers
   size_t dz_bytes;     // one dZ band buffer
   size_t flag_bytes;   // one flag grid
+  bool compact;        // ignored rows compacted away (row map in the workspace)
+  int ncblk;           // compaction blocks
+  size_t off_rowmap, off_cblk;
   size_t off_zy, off_bsum, off_bcnt, off_flags, off_flagsT, off_big, total;
 };
 
@@ -58,7 +61,12 @@ int validate(const flce_desc* d) {
   if (d->hidden < 8 || d->hidden % 8 != 0 || d->hidden >= (int64_t(1) << 20)) return FLCE_E_SHAPE;
   if (d->in_dtype != FLCE_BF16 && d->in_dtype != FLCE_F32) return FLCE_E_DTYPE;
   if (d->reduction < FLCE_MEAN || d->reduction > FLCE_NONE) return FLCE_E_UNSUPPORTED;
-  if (d->flags & ~uint32_t(FLCE_FLAG_PROFILE)) return FLCE_E_UNSUPPORTED;
+  if (d->flags & ~uint32_t(FLCE_FLAG_PROFILE | FLCE_FLAG_COMPACT_IGNORED)) return FLCE_E_UNSUPPORTED;
+  if (d->flags & FLCE_FLAG_COMPACT_IGNORED) {
+    // bf16 core only; gathered H rows and scattered dH rows use 32-bit byte offsets
+    if (d->in_dtype != FLCE_BF16) return FLCE_E_UNSUPPORTED;
+    if (d->n_rows * d->hidden * 4 >= (int64_t(1) << 31)) return FLCE_E_UNSUPPORTED;
+  }
   if (!(d->filter_eps >= 0.f) || !std::isfinite(d->filter_eps)) return FLCE_E_UNSUPPORTED;
   return FLCE_OK;
 }
@@ -82,6 +90,13 @@ size_t layout(Plan& p) {
   o += 2 * p.flag_bytes;
   p.off_flagsT = o;
   o += 2 * p.flag_bytes;
+  p.off_rowmap = o;
+  p.off_cblk = o;
+  if (p.compact) {
+    o = align256(o + N * 4);
+    p.off_cblk = o;
+    o = align256(o + size_t(p.ncblk) * 4);
+  }
   p.off_big = o;
   p.dz_bytes = align256(size_t(p.NS) * p.VS * p.es);
   p.big = std::max(2 * p.dz_bytes, size_t(2) * p.Tv * p.NF * 4);
@@ -107,6 +122,8 @@ int make_plan(const flce_desc* d, Plan& p) {
   p.V = d->vocab;
   p.dtype = d->in_dtype;
   p.es = d->in_dtype == FLCE_BF16 ? 2 : 4;
+  p.compact = (d->flags & FLCE_FLAG_COMPACT_IGNORED) != 0;
+  p.ncblk = int(cdiv(std::max<int64_t>(p.N, 1), flce::kCompactRows));
   p.Tv = int(cdiv(p.V, flce::kTile));
   const int64_t Npad = cdiv(std::max<int64_t>(p.N, 1), 256) * 256;
   p.nblk = int(cdiv(std::max<int64_t>(p.N, 1), flce::kCombineRows));   // one per combine block
@@ -200,6 +217,8 @@ struct Ws {
   int* bcnt;
   uint8_t *flags[2], *flagsT[2];
   char* dz[2];
+  int* rowmap;   // null without compaction
+  int* cblk;
 };
 
 Ws carve(const Plan& p, void* ws) {
@@ -210,12 +229,31 @@ Ws carve(const Plan& p, void* ws) {
   w.zy = reinterpret_cast<float*>(b + p.off_zy);
   w.bsum = reinterpret_cast<double*>(b + p.off_bsum);
   w.bcnt = reinterpret_cast<int*>(b + p.off_bcnt);
+  w.rowmap = p.compact ? reinterpret_cast<int*>(b + p.off_rowmap) : nullptr;
+  w.cblk = reinterpret_cast<int*>(b + p.off_cblk);
   for (int k = 0; k < 2; ++k) {
     w.flags[k] = reinterpret_cast<uint8_t*>(b + p.off_flags + k * p.flag_bytes);
     w.flagsT[k] = reinterpret_cast<uint8_t*>(b + p.off_flagsT + k * p.flag_bytes);
     w.dz[k] = b + p.off_big + k * p.dz_bytes;
   }
   return w;
+}
+
+// Row map of the non-ignored rows, then the ignored ones (CCE App. B: ignored
+// tokens removed before any contraction); hdr->nvalid counts the former.
+int run_compact(const flce_desc* d, const Plan& p, const int64_t* y, const Ws& w, bool prof,
+                hipStream_t s) {
+  const int N = int(p.N);
+  FLCE_TRY(launch(FLCE_K_AUX, prof, s, [&] {
+    flce::compact_count_kernel<<<dim3(p.ncblk), dim3(256), 0, s>>>(y, N, d->ignore_index, w.cblk);
+  }));
+  FLCE_TRY(launch(FLCE_K_AUX, prof, s, [&] {
+    flce::compact_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(w.cblk, p.ncblk, w.hdr);
+  }));
+  return launch(FLCE_K_AUX, prof, s, [&] {
+    flce::compact_scatter_kernel<<<dim3(p.ncblk), dim3(256), 0, s>>>(y, N, d->ignore_index, w.cblk,
+                                                                    w.hdr, w.rowmap);
+  });
 }
 
 template <typename T>
@@ -231,12 +269,12 @@ int run_forward(const flce_desc* d, const Plan& p, const void* H, const void* W,
     FLCE_TRY(launch(FLCE_K_FWD_LSE, prof, s, [&] {
       flce::fwd_lse_kernel<T><<<dim3(p.Tv * TNn), dim3(flce::kThreads), 0, s>>>(
           static_cast<const T*>(H), static_cast<const T*>(W), y, N, D, V, d->ignore_index, nb0,
-          ns, p.Tv, TNn, pm, ps, w.zy, w.hdr);
+          ns, p.Tv, TNn, pm, ps, w.zy, w.hdr, w.rowmap);
     }));
     FLCE_TRY(launch(FLCE_K_LSE_COMBINE, prof, s, [&] {
       flce::lse_combine_kernel<<<dim3(int(cdiv(ns, flce::kCombineRows))), dim3(256), 0, s>>>(
           pm, ps, w.zy, y, N, V, p.Tv, nb0, ns, d->ignore_index, lse, loss_rows, w.bsum, w.bcnt,
-          w.hdr);
+          w.hdr, w.rowmap);
     }));
   }
   FLCE_TRY(launch(FLCE_K_FINALIZE, prof, s, [&] {
@@ -272,6 +310,11 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
   const int N = int(p.N), D = int(p.D), V = int(p.V);
   const int Td = int(cdiv(D, flce::kTile));
   const int nb = p.nbn * p.nbv;
+  if (w.rowmap)   // dH rows of ignored rows: no tile writes them
+    FLCE_TRY(launch(FLCE_K_AUX, prof, s, [&] {
+      flce::zero_ignored_rows_kernel<<<dim3(int(cdiv(N, 16))), dim3(256), 0, s>>>(w.rowmap, w.hdr,
+                                                                                N, D, dH);
+    }));
   for (int k = 0; k <= nb; ++k) {
     flce::DzArgs<T> da{};
     flce::GradArgs<T> ga{};
@@ -283,7 +326,7 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
       da = flce::DzArgs<T>{static_cast<const T*>(H), static_cast<const T*>(W), y, lse, dloss_rows,
                            w.hdr, N, D, V, d->ignore_index, d->reduction, d->filter_eps, band,
                            TMv, TNn, reinterpret_cast<T*>(w.dz[k & 1]), w.flags[k & 1],
-                           w.flagsT[k & 1]};
+                           w.flagsT[k & 1], w.rowmap};
       g_dz = TMv * TNn;
     }
     if (k > 0) {
@@ -294,7 +337,7 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
       ga = flce::GradArgs<T>{static_cast<const T*>(H), static_cast<const T*>(W),
                              reinterpret_cast<const T*>(w.dz[(k - 1) & 1]), w.flags[(k - 1) & 1],
                              w.flagsT[(k - 1) & 1], dH, dW, N, D, V, band, T3n, T2n, Td,
-                             bv > 0 ? 1 : 0, bn > 0 ? 1 : 0};
+                             bv > 0 ? 1 : 0, bn > 0 ? 1 : 0, w.rowmap, w.hdr};
       // the contraction with the longer K (dH^T: band vocabulary, dW^T: band rows) first
       h_first = band.vs_cur >= band.ns_cur ? 1 : 0;
       g_long = Td * (h_first ? T3n : T2n);
@@ -303,10 +346,20 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
     const int cls = k == 0 ? FLCE_K_BWD_DZ : (k == nb ? FLCE_K_BWD_GRAD : FLCE_K_BWD_BAND);
     FLCE_TRY(launch(cls, prof, s, [&] {
       const dim3 grid(g_grad + g_dz), block(flce::kThreads);
-      if (d->filter_eps > 0.f)
-        flce::bwd_band_kernel<T, true><<<grid, block, 0, s>>>(ga, da, g_long, g_grad, h_first);
+      const bool filt = d->filter_eps > 0.f;
+      if constexpr (sizeof(T) == 2) {
+        if (w.rowmap) {
+          if (filt)
+            flce::bwd_band_kernel<T, true, true><<<grid, block, 0, s>>>(ga, da, g_long, g_grad, h_first);
+          else
+            flce::bwd_band_kernel<T, false, true><<<grid, block, 0, s>>>(ga, da, g_long, g_grad, h_first);
+          return;
+        }
+      }
+      if (filt)
+        flce::bwd_band_kernel<T, true, false><<<grid, block, 0, s>>>(ga, da, g_long, g_grad, h_first);
       else
-        flce::bwd_band_kernel<T, false><<<grid, block, 0, s>>>(ga, da, g_long, g_grad, h_first);
+        flce::bwd_band_kernel<T, false, false><<<grid, block, 0, s>>>(ga, da, g_long, g_grad, h_first);
     }));
   }
   return FLCE_OK;
@@ -375,6 +428,7 @@ int flce_forward(const flce_desc* d, const void* H, const void* W, const int64_t
       flce::clear_status_kernel<<<1, 64, 0, stream>>>(w.hdr, d->reduction != FLCE_NONE ? loss : nullptr);
     });
   }
+  if (p.compact) FLCE_TRY(run_compact(d, p, y, w, prof, stream));
   if (p.dtype == FLCE_BF16)
     return run_forward<uint16_t>(d, p, H, W, y, loss_rows, lse, loss, w, prof, stream);
   return run_forward<float>(d, p, H, W, y, loss_rows, lse, loss, w, prof, stream);
@@ -401,6 +455,7 @@ int flce_backward(const flce_desc* d, const void* H, const void* W, const int64_
     flce::bwd_prep_kernel<<<dim3(1), dim3(256), 0, stream>>>(y, int(p.N), int(p.V), d->ignore_index,
                                                              d->reduction, dloss, w.hdr);
   }));
+  if (p.compact) FLCE_TRY(run_compact(d, p, y, w, prof, stream));
   const float* drows = d->reduction == FLCE_NONE ? dloss : nullptr;
   if (p.dtype == FLCE_BF16)
     return run_bands<uint16_t>(d, p, H, W, y, lse, drows, dH, dW, w, prof, stream);
@@ -426,6 +481,7 @@ int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const i
     }));
     return zero_dW(p, dW, prof, stream);
   }
+  if (p.compact) FLCE_TRY(run_compact(d, p, y, w, prof, stream));
   if (p.dtype == FLCE_BF16) {
     FLCE_TRY(run_forward<uint16_t>(d, p, H, W, y, loss_rows, lse, loss, w, prof, stream));
     return run_bands<uint16_t>(d, p, H, W, y, lse, nullptr, dH, dW, w, prof, stream);

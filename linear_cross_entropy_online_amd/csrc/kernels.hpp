@@ -30,8 +30,13 @@ struct Header {           // first 256 bytes of the workspace
   int status;             // bit 0: target outside [0, V) and != ignore_index
   int count;              // non-ignored rows
   float gscale;           // g for mean / sum: dloss / max(count, 1) or dloss
-  float pad[61];
+  int nvalid;             // with row compaction: rows whose target is not ignore_index
+  float pad[60];
 };
+
+// The LDS row table of a compacted dW^T contraction holds NS / 2 entries per
+// parity, i.e. 32 per 64-row filter block of the band.
+constexpr int kFilterHalfPerBlock = 32;
 
 // K elements of one pass of a tile contraction: 64 for bf16 (LDS-DMA core,
 // whole 128-byte lines per operand row), 32 for fp32 (register-staged core).
@@ -41,7 +46,7 @@ constexpr int step_k() { return sizeof(T) == 2 ? kDmaKStep : 32; }
 // A 256x256 tile contraction over K = [0, K): bf16 through the LDS-DMA core,
 // fp32 through the register-staged core.  active(s) covers K
 // [s step_k, (s + 1) step_k).
-template <typename T, bool AT, bool BT, class Active>
+template <typename T, bool AT, bool BT, class Active, bool GATHER_A = false>
 __device__ __forceinline__ void tile_contract(const Operand& A, const Operand& B, int m0, int n0,
                                               int K, const Active& active, f32x16 (&acc)[4][4],
                                               char* lds) {
@@ -52,8 +57,9 @@ __device__ __forceinline__ void tile_contract(const Operand& A, const Operand& B
   // block is shared by 8 consecutive B tiles, a B block by 4 consecutive A
   // tiles, and consecutive tiles have distinct residues.
   if constexpr (sizeof(T) == 2)
-    gemm_tile_dma<AT, BT>(A, B, m0, n0, nsteps, active, acc, lds,
-                          L2Split{(n0 / kTile) & 7, 8}, L2Split{(m0 / kTile) & 3, 4});
+    gemm_tile_dma<AT, BT, Active, GATHER_A>(A, B, m0, n0, nsteps, active, acc, lds,
+                                             L2Split{(n0 / kTile) & 7, 8},
+                                             L2Split{(m0 / kTile) & 3, 4});
   else gemm_tile<T, AT, BT>(A, B, m0, n0, nsteps, active, acc, lds);
 }
 
@@ -129,17 +135,21 @@ __global__ void __launch_bounds__(kThreads, 1)
 fwd_lse_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* __restrict__ y,
                int N, int D, int V, int64_t ignore, int nb0, int ns, int TMv, int TNn,
                float* __restrict__ part_m, float* __restrict__ part_s, float* __restrict__ zy,
-               Header* __restrict__ hdr) {
+               Header* __restrict__ hdr, const int* __restrict__ rowmap) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   if (nb0 == 0 && blockIdx.x == 0 && threadIdx.x == 0) hdr->status = 0;   // start of a forward
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   int tm, tn;
   grouped_tile(t, TMv, TNn, 4, tm, tn);
   const int v0 = tm * kTile, n0 = nb0 + tn * kTile;
+  // rows are compacted positions when rowmap is given (the row itself is
+  // rowmap[c]); tiles past the non-ignored rows have nothing to do
+  const int nval = rowmap ? hdr->nvalid : N;
+  if (n0 >= nval) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const Operand A{reinterpret_cast<const char*>(W), D, V, D};
-  const Operand B{reinterpret_cast<const char*>(H), D, N, D};
+  const Operand B{reinterpret_cast<const char*>(H), D, nval, D, rowmap};
   f32x16 acc[4][4];
   tile_contract<T, false, false>(A, B, v0, n0, D, AllActive{}, acc, lds);
 
@@ -147,8 +157,9 @@ fwd_lse_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* 
   int rel[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 128 + j * 32 + (lane & 31);
-    const int64_t yy = n < N ? y[n] : ignore;
+    const int c = n0 + wn * 128 + j * 32 + (lane & 31);
+    const int n = c < nval ? (rowmap ? rowmap[c] : c) : -1;
+    const int64_t yy = n >= 0 ? y[n] : ignore;
     rel[j] = (yy >= 0 && yy < V) ? (int)(yy - vw) : -1;
   }
   if (vw + 128 > V) mask_rows(acc, vw, V, lane, -INFINITY);   // last vocabulary tile
@@ -222,14 +233,18 @@ lse_combine_kernel(const float* __restrict__ part_m, const float* __restrict__ p
                    const float* __restrict__ zy, const int64_t* __restrict__ y, int N, int V,
                    int Tv, int nb0, int ns, int64_t ignore, float* __restrict__ lse,
                    float* __restrict__ loss_rows, double* __restrict__ blk_sum,
-                   int* __restrict__ blk_cnt, Header* __restrict__ hdr) {
+                   int* __restrict__ blk_cnt, Header* __restrict__ hdr,
+                   const int* __restrict__ rowmap) {
   __shared__ float sh_m[16][kCombineRows], sh_sum[16][kCombineRows];
   __shared__ double sh_s[256];
   __shared__ int sh_c[256];
   const int r = threadIdx.x % kCombineRows, sl = threadIdx.x / kCombineRows;
   const int nl = blockIdx.x * kCombineRows + r;   // row within the band
+  // with compaction, positions past the non-ignored rows hold the ignored
+  // rows: no partials were made for them, their outputs are 0
+  const bool live = nl < ns && (!rowmap || nb0 + nl < hdr->nvalid);
   float M = -INFINITY, S = 0.f;
-  if (nl < ns) {
+  if (live) {
     for (int k = sl; k < Tv; k += 16) {
       const float m = part_m[(int64_t)k * ns + nl], sk = part_s[(int64_t)k * ns + nl];
       if (m == -INFINITY) continue;
@@ -246,14 +261,20 @@ lse_combine_kernel(const float* __restrict__ part_m, const float* __restrict__ p
   __syncthreads();
   double s = 0.0;
   int c = 0;
-  if (sl == 0 && nl < ns) {
+  if (sl == 0 && nl < ns && !live) {
+    const int n = rowmap[nb0 + nl];
+    lse[n] = 0.f;
+    loss_rows[n] = 0.f;
+  }
+  if (sl == 0 && live) {
     float Mx = -INFINITY;
     for (int q = 0; q < 16; ++q) Mx = fmaxf(Mx, sh_m[q][r]);
     float St = 0.f;
     for (int q = 0; q < 16; ++q)
       St += sh_sum[q][r] * fast_exp2((sh_m[q][r] - Mx) * kLog2e);
     const float l = Mx + fast_log2(St) * kLn2;
-    const int n = nb0 + nl;
+    const int pos = nb0 + nl;                   // position (zy is by position)
+    const int n = rowmap ? rowmap[pos] : pos;   // row
     lse[n] = l;
     const int64_t yy = y[n];
     float lr = 0.f;
@@ -263,7 +284,7 @@ lse_combine_kernel(const float* __restrict__ part_m, const float* __restrict__ p
         lr = __builtin_nanf("");
         atomicOr(&hdr->status, 1);
       } else {
-        lr = l - zy[n];
+        lr = l - zy[pos];
       }
     }
     loss_rows[n] = lr;
@@ -321,6 +342,104 @@ bwd_prep_kernel(const int64_t* __restrict__ y, int N, int V, int64_t ignore, int
     hdr->status = s > 0.0 ? 1 : 0;
     hdr->count = c;
     hdr->gscale = reduction == 0 ? up / (float)cl : up;
+  }
+}
+
+// ------------------------------------------------- ignored-row compaction ----
+// rowmap lists the rows whose target is not ignore_index, in order, then the
+// ignored rows, in order; hdr->nvalid counts the former.  Blocks of
+// kCompactRows rows: count, one-block exclusive scan of the counts, scatter.
+constexpr int kCompactRows = 1024;
+
+__device__ __forceinline__ int block_sum_256(int v, int* sh) {
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  const int r = sh[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(256)
+compact_count_kernel(const int64_t* __restrict__ y, int N, int64_t ignore, int* __restrict__ blk) {
+  __shared__ int sh[256];
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = blockIdx.x * kCompactRows + threadIdx.x * 4 + i;
+    c += (n < N && y[n] != ignore) ? 1 : 0;
+  }
+  const int tot = block_sum_256(c, sh);
+  if (threadIdx.x == 0) blk[blockIdx.x] = tot;
+}
+
+// blk[b] <- valid rows in blocks before b; hdr->nvalid <- all valid rows
+__global__ void __launch_bounds__(1024)
+compact_scan_kernel(int* __restrict__ blk, int nblk, Header* __restrict__ hdr) {
+  __shared__ int sh[1024];
+  int carry = 0;
+  for (int base = 0; base < nblk; base += 1024) {
+    const int i = base + (int)threadIdx.x;
+    const int v = i < nblk ? blk[i] : 0;
+    sh[threadIdx.x] = v;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan (Hillis-Steele)
+      const int a = (int)threadIdx.x >= o ? sh[threadIdx.x - o] : 0;
+      __syncthreads();
+      sh[threadIdx.x] += a;
+      __syncthreads();
+    }
+    if (i < nblk) blk[i] = carry + sh[threadIdx.x] - v;
+    carry += sh[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) hdr->nvalid = carry;
+}
+
+__global__ void __launch_bounds__(256)
+compact_scatter_kernel(const int64_t* __restrict__ y, int N, int64_t ignore,
+                       const int* __restrict__ blk, const Header* __restrict__ hdr,
+                       int* __restrict__ rowmap) {
+  __shared__ int sh[256];
+  const int b = blockIdx.x, t = threadIdx.x;
+  bool f[4];
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = b * kCompactRows + t * 4 + i;
+    f[i] = n < N && y[n] != ignore;
+    c += f[i] ? 1 : 0;
+  }
+  sh[t] = c;   // exclusive scan of the per-thread counts
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int a = t >= o ? sh[t - o] : 0;
+    __syncthreads();
+    sh[t] += a;
+    __syncthreads();
+  }
+  const int before = sh[t] - c;                    // valid rows of this block before thread t
+  int pv = blk[b] + before;                        // next position of a valid row
+  int pi = hdr->nvalid + (b * kCompactRows - blk[b]) + (t * 4 - before);   // of an ignored row
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = b * kCompactRows + t * 4 + i;
+    if (n < N) rowmap[f[i] ? pv++ : pi++] = n;
+  }
+}
+
+// dH rows of the ignored rows (positions nvalid .. N of rowmap) <- 0
+__global__ void __launch_bounds__(256)
+zero_ignored_rows_kernel(const int* __restrict__ rowmap, const Header* __restrict__ hdr, int N,
+                         int D, float* __restrict__ dH) {
+  const int c0 = blockIdx.x * 16;
+  const int nval = hdr->nvalid;
+  for (int c = c0 > nval ? c0 : nval; c < c0 + 16 && c < N; ++c) {
+    f32x4* row = reinterpret_cast<f32x4*>(dH + (int64_t)rowmap[c] * D);
+    for (int i = threadIdx.x; i < D / 4; i += 256) row[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -387,6 +506,7 @@ struct DzArgs {
   T* dz;                 // the band's dZ buffer [ns][ldz]
   uint8_t* flags;        // [frows][fcols]
   uint8_t* flagsT;       // [fcols][frows]
+  const int* rowmap;     // row compaction: band rows are positions of rowmap (else rows)
 };
 
 // dZ tile t of a band: Z = W_v H_n^T recomputed, G = softmax(Z) - onehot(y),
@@ -406,14 +526,17 @@ __device__ __forceinline__ void dz_tile(const DzArgs<T>& a, int t, char* lds) {
   T* __restrict__ dz = a.dz;
   uint8_t* __restrict__ flags = a.flags;
   uint8_t* __restrict__ flagsT = a.flagsT;
+  const int* __restrict__ rowmap = a.rowmap;
   int tm, tn;
   grouped_tile(t, TMv, TNn, 4, tm, tn);
   const int v0 = band.vb0 + tm * kTile, n0 = band.nb0 + tn * kTile;
+  const int nval = rowmap ? a.hdr->nvalid : N;
+  if (n0 >= nval) return;   // only ignored rows: the contractions do not read them
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
   const Operand A{reinterpret_cast<const char*>(W), D, V, D};
-  const Operand B{reinterpret_cast<const char*>(H), D, N, D};
+  const Operand B{reinterpret_cast<const char*>(H), D, nval, D, rowmap};
   f32x16 acc[4][4];
   tile_contract<T, false, false>(A, B, v0, n0, D, AllActive{}, acc, lds);
 
@@ -424,8 +547,9 @@ __device__ __forceinline__ void dz_tile(const DzArgs<T>& a, int t, char* lds) {
   const int vw = v0 + wm * 128;  // first vocabulary row of this wave's block
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 128 + j * 32 + (lane & 31);
-    const bool in = n < N;
+    const int c = n0 + wn * 128 + j * 32 + (lane & 31);
+    const bool in = c < nval;
+    const int n = in ? (rowmap ? rowmap[c] : c) : 0;
     const int64_t yy = in ? y[n] : ignore;
     const bool valid = in && yy != ignore;
     bad[j] = valid && (yy < 0 || yy >= V);
@@ -612,10 +736,17 @@ struct GradArgs {
   BandArgs band;
   int T3n, T2n, Td;        // token-row tiles, vocabulary tiles, d tiles of the band
   int beta_h, beta_w;      // accumulate into dH / dW (else overwrite)
+  const int* rowmap;       // row compaction (COMPACT): band rows are positions of rowmap
+  const Header* hdr;       // nvalid with row compaction
 };
 
 // Gradient tile `local` of one of the band's two contractions (is_h: dH^T).
-template <typename T, bool FILTER>
+// COMPACT: the band's rows are positions of a.rowmap; only the first
+// nvalid - nb0 of them are rows (the rest are ignored rows, whose dZ rows are
+// not made): dH^T tiles past them exit, their rows are scattered through the
+// map, and dW^T contracts over them only, gathering H's rows through an LDS
+// copy of the map.
+template <typename T, bool FILTER, bool COMPACT = false>
 __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int local, char* lds) {
   const T* __restrict__ H = a.H;
   const T* __restrict__ W = a.W;
@@ -632,8 +763,11 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
   f32x16 acc[4][4];
   float* out;
   int rvalid, beta, td, tr;
+  // rows of the band that are rows (all of them without compaction)
+  const int nrows = COMPACT ? min(band.ns_cur, a.hdr->nvalid - band.nb0) : band.ns_cur;
   if (is_h) {
     grouped_tile(local, Td, T3n, 4, td, tr);   // d tile, band row tile
+    if (COMPACT && tr * kTile >= nrows) return;   // ignored rows only: zeroed separately
     const Operand A{reinterpret_cast<const char*>(W + (int64_t)band.vb0 * D), D, D, band.vs_cur};
     const int kpad = (band.vs_cur + kTile - 1) / kTile * kTile;
     const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T3n * kTile, kpad};
@@ -644,17 +778,37 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
       tile_contract<T, true, false>(A, B, td * kTile, tr * kTile, band.vs_cur, AllActive{}, acc, lds);
     }
     out = dH + (int64_t)band.nb0 * D;
-    rvalid = band.ns_cur;
+    rvalid = COMPACT ? nrows : band.ns_cur;
     beta = beta_h;
   } else {
     grouped_tile(local, Td, T2n, 4, td, tr);   // d tile, band vocabulary tile
-    const Operand A{reinterpret_cast<const char*>(H + (int64_t)band.nb0 * D), D, D, band.ns_cur};
-    const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2n * kTile, band.ns_cur};
-    if constexpr (FILTER) {
-      const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols};
-      tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, act, acc, lds);
+    const int K = nrows > 0 ? nrows : 0;
+    if constexpr (COMPACT) {
+      char* table = lds + kDmaLdsBytes + 256;
+      const int half = band.frows * kFilterHalfPerBlock;   // NS / 2 entries per parity
+      gather_table(table, a.rowmap + band.nb0, K, half);
+      const Operand A{reinterpret_cast<const char*>(H), D, D, K,
+                      reinterpret_cast<const int*>(table), half};
+      const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2n * kTile, K};
+      if constexpr (FILTER) {
+        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols};
+        tile_contract<T, true, true, SkipRowsOfFlags<step_k<T>()>, true>(A, B, td * kTile,
+                                                                        tr * kTile, K, act, acc,
+                                                                        lds);
+      } else {
+        tile_contract<T, true, true, AllActive, true>(A, B, td * kTile, tr * kTile, K, AllActive{},
+                                                      acc, lds);
+      }
     } else {
-      tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, AllActive{}, acc, lds);
+      const Operand A{reinterpret_cast<const char*>(H + (int64_t)band.nb0 * D), D, D, band.ns_cur};
+      const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2n * kTile, band.ns_cur};
+      if constexpr (FILTER) {
+        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols};
+        tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, act, acc, lds);
+      } else {
+        tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, AllActive{}, acc,
+                                     lds);
+      }
     }
     out = dW + (int64_t)band.vb0 * D;
     rvalid = band.vs_cur;
@@ -666,21 +820,25 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
   // the 16 loads of a row group go out together, with no branches between
   // them.
   const int row0 = tr * kTile;
-  const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(reinterpret_cast<const char*>(out + (int64_t)row0 * D));
+  // with compaction the dH^T tile's rows are scattered through the map:
+  // offsets from the start of dH (below 2^31 by the planner's check)
+  const bool scatter = COMPACT && is_h;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(
+      scatter ? dH : out + (int64_t)row0 * D));
   const int dw = td * kTile + wm * 128 + 4 * (lane >> 5);
   const int lw = wn * 128 + (lane & 31);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int lr = lw + 32 * j;
     const bool rok = row0 + lr < rvalid;
+    const int64_t orow = scatter ? (rok ? (int64_t)a.rowmap[band.nb0 + row0 + lr] : 0) : lr;
     uint32_t off[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int d = dw + 32 * i + 8 * q;
-        off[i][q] = rok && d < D ? (uint32_t)(((int64_t)lr * D + d) * 4) : kOob;
+        off[i][q] = rok && d < D ? (uint32_t)((orow * D + d) * 4) : kOob;
       }
     f32x4 old[4][4];
 #pragma unroll
@@ -708,10 +866,13 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
 // Tile kinds, longest first on every XCD: [0, g_long) gradient tiles of the
 // contraction with the longer K, [g_long, g_grad) the other gradient tiles,
 // [g_grad, G) dZ tiles.
-template <typename T, bool FILTER>
+constexpr int kBandLdsCompact = kDmaLdsBytes + 256 + kGatherTableBytes;   // slots, line touch, map
+
+template <typename T, bool FILTER, bool COMPACT>
 __global__ void __launch_bounds__(kThreads, 1)
 bwd_band_kernel(GradArgs<T> ga, DzArgs<T> da, int g_long, int g_grad, int h_first) {
-  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char
+      lds[COMPACT && kBandLdsCompact > kLdsBytes ? kBandLdsCompact : kLdsBytes];
   const int t = xcd_remap_kinds(blockIdx.x, gridDim.x, g_long, g_grad);
   if (t >= g_grad) {
     dz_tile<T>(da, t - g_grad, lds);
@@ -720,7 +881,7 @@ bwd_band_kernel(GradArgs<T> ga, DzArgs<T> da, int g_long, int g_grad, int h_firs
   const int T3 = ga.Td * ga.T3n;   // dH^T tiles
   const bool is_h = h_first ? t < T3 : t >= g_long;
   const int local = h_first ? (is_h ? t : t - T3) : (is_h ? t - g_long : t);
-  grad_tile<T, FILTER>(ga, is_h, local, lds);
+  grad_tile<T, FILTER, COMPACT>(ga, is_h, local, lds);
 }
 
 }  // namespace flce

@@ -37,6 +37,8 @@
 // exactly for the stage it is about to read.
 #pragma once
 
+#include <type_traits>
+
 #include "tile_mma.hpp"
 
 #pragma clang diagnostic push
@@ -52,6 +54,7 @@ constexpr int kDmaStageBytes = 2 * kDmaOpBytes;  // A + B
 constexpr int kDmaLdsBytes = kDmaSlots * kDmaStageBytes;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -107,8 +110,10 @@ struct DmaNatural {
   int kc[2];              // K element offset of this lane's chunk, by q parity
   const char* base;       // element (m0, 0)
   int64_t ld, kext, mrem;
+  bool gather;            // rows through op.rowmap (no line prefetch then)
   __device__ __forceinline__ void init(const Operand& op, int m0, int wave, int lane) {
-    base = op.base + (int64_t)m0 * op.ld * 2;
+    gather = op.rowmap != nullptr;
+    base = gather ? op.base : op.base + (int64_t)m0 * op.ld * 2;
     ld = op.ld;
     kext = op.kext;
     mrem = op.mext - m0;
@@ -117,8 +122,9 @@ struct DmaNatural {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int row = 8 * (8 * wave + q) + (lane >> 3);
-      off[q] = (int64_t)m0 + row < op.mext ? (uint32_t)(((int64_t)row * op.ld + kc[q & 1]) * 2)
-                                           : kOob;
+      const bool in = (int64_t)m0 + row < op.mext;
+      const int64_t r = gather ? (in ? (int64_t)op.rowmap[m0 + row] : 0) : row;
+      off[q] = in ? (uint32_t)((r * op.ld + kc[q & 1]) * 2) : kOob;
     }
   }
   __device__ __forceinline__ void issue(uint32_t lds_op, int k0, int wave) const {
@@ -143,7 +149,7 @@ struct DmaNatural {
                                            bool on) const {
     const int per = kTile / sp.nshare;
     const int row = sp.share * per + (lane & (per - 1));
-    const bool ok = on && row < mrem && k0 < kext;
+    const bool ok = on && !gather && row < mrem && k0 < kext;
     dma4(lds_dummy, ok ? (uint32_t)((int64_t)row * ld * 2) : kOob,
          make_rsrc(base + (int64_t)k0 * 2));
   }
@@ -207,6 +213,87 @@ struct DmaTransposed {
 template <bool TRANS> struct DmaLoader;
 template <> struct DmaLoader<false> : DmaNatural {};
 template <> struct DmaLoader<true> : DmaTransposed {};
+
+// transposed [k][m] operand whose k rows are gathered: op.rowmap points at
+// an LDS table (built by the caller before the contraction) that holds the
+// operand's row indices split by parity, table[h][j] = row of k = 2 j + h,
+// `table_half` entries per parity.  A lane loads k rows k0 + 16 w + 2 q + h
+// (h = lane / 32, q = 0..7), so its eight indices of a stage are eight
+// consecutive entries of table[h]: two 16-byte LDS reads, issued by rows()
+// before the barrier that precedes the stage's DMAs.
+constexpr int kGatherTableBytes = 16384;   // 4096 rows
+struct DmaTransposedGather {
+  uint32_t col[8];        // this lane's byte column (m) for instruction q
+  bool colok[8];
+  const char* base;       // element (0, m0)
+  const char* table;      // LDS table (generic pointer into LDS)
+  int table_half;
+  int64_t ld, kext, mrem;
+  int krow0;              // 16 w + L / 32
+  int wave16;             // 16 w
+  int idx[8];             // row of k0 + 16 w + 2 q + h, per q
+  bool gather = true;
+  __device__ __forceinline__ void init(const Operand& op, int m0, int wave, int lane) {
+    base = op.base + (int64_t)m0 * 2;
+    table = reinterpret_cast<const char*>(op.rowmap);
+    table_half = op.rowmap_half;
+    ld = op.ld;
+    kext = op.kext;
+    mrem = op.mext - m0;
+    wave16 = 16 * wave;
+    krow0 = wave16 + (lane >> 5);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int krow = krow0 + 2 * q;
+      const int seg = ((lane & 31) >> 1) ^ (2 * (krow & 3));
+      const int m = seg * 16 + (lane & 1) * 8;
+      colok[q] = (int64_t)m0 + m < op.mext;
+      col[q] = (uint32_t)(m * 2);
+    }
+  }
+  __device__ __forceinline__ void rows(int k0) {
+    typedef __attribute__((address_space(3))) const i32x4 lds_i32x4;
+    const int h = (threadIdx.x >> 5) & 1;
+    lds_i32x4* p = (lds_i32x4*)(lds_char*)(table + (h * table_half + ((k0 + wave16) >> 1)) * 4);
+    const i32x4 lo = p[0], hi = p[1];
+    idx[0] = lo.x; idx[1] = lo.y; idx[2] = lo.z; idx[3] = lo.w;
+    idx[4] = hi.x; idx[5] = hi.y; idx[6] = hi.z; idx[7] = hi.w;
+  }
+  __device__ __forceinline__ void rows_wait() {}
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int) const { return make_rsrc(base); }
+  template <int Q>
+  __device__ __forceinline__ void issue_q(uint32_t lds_op, int k0, int wave, bool more,
+                                          __amdgpu_buffer_rsrc_t rs) const {
+    const bool ok = more && colok[Q] && (k0 + krow0 + 2 * Q < kext);
+    const uint32_t o = (uint32_t)idx[Q] * (uint32_t)(ld * 2) + col[Q];   // < 2^31
+    dma16(lds_op + (8 * wave + Q) * 1024, ok ? o : kOob, rs);
+  }
+  __device__ __forceinline__ void issue(uint32_t lds_op, int k0, int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(k0);
+    issue_q<0>(lds_op, k0, wave, true, rs);
+    issue_q<1>(lds_op, k0, wave, true, rs);
+    issue_q<2>(lds_op, k0, wave, true, rs);
+    issue_q<3>(lds_op, k0, wave, true, rs);
+    issue_q<4>(lds_op, k0, wave, true, rs);
+    issue_q<5>(lds_op, k0, wave, true, rs);
+    issue_q<6>(lds_op, k0, wave, true, rs);
+    issue_q<7>(lds_op, k0, wave, true, rs);
+  }
+  __device__ __forceinline__ void prefetch(uint32_t lds_dummy, int, L2Split, int, bool) const {
+    dma4(lds_dummy, kOob, make_rsrc(base));   // keeps the per-wave load count; touches nothing
+  }
+};
+
+// Fills the LDS gather table of a transposed gathered operand from the global
+// row indices rowmap[0 .. rows) (zeros after them, up to `half` entries per
+// parity); every thread of the workgroup takes part, and a barrier follows.
+__device__ __forceinline__ void gather_table(char* lds_table, const int* rowmap, int rows,
+                                             int half) {
+  int* t = reinterpret_cast<int*>(lds_table);
+  for (int k = threadIdx.x; k < 2 * half; k += blockDim.x)
+    t[(k & 1) * half + (k >> 1)] = k < rows ? rowmap[k] : 0;
+  __syncthreads();
+}
 
 // ----------------------------------------------------------- fragments ----
 // Fragments of MFMA K sub-step KS (0..3) of a stage for the wave's 4 blocks.
@@ -313,10 +400,10 @@ __device__ __forceinline__ void mfma_group(f32x16 (&acc)[4][4], const bf16x8 (&a
 // (P / 2, 2 (P % 2)) and (P / 2, 2 (P % 2) + 1)}, pinned in that order so
 // that a DMA instruction that has to wait for the address unit does not hold
 // back more than the MFMAs already issued.
-template <int P, bool AT, bool BT>
+template <int P, bool AT, bool BT, class LA, class LB>
 __device__ __forceinline__ void last_substep(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
-                                             const bf16x8 (&b)[4], const DmaLoader<AT>& la,
-                                             const DmaLoader<BT>& lb, uint32_t la_op,
+                                             const bf16x8 (&b)[4], const LA& la,
+                                             const LB& lb, uint32_t la_op,
                                              uint32_t lb_op, int k0, bool more, int wave,
                                              __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb,
                                              const FragReader<AT>& fa, const FragReader<BT>& fb,
@@ -332,8 +419,8 @@ __device__ __forceinline__ void last_substep(f32x16 (&acc)[4][4], const bf16x8 (
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     acc[i][j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j + 1], acc[i][j + 1], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    last_substep<P + 1, AT, BT>(acc, a, b, la, lb, la_op, lb_op, k0, more, wave, rsa, rsb, fa, fb,
-                                sn, an, bn);
+    last_substep<P + 1, AT, BT, LA, LB>(acc, a, b, la, lb, la_op, lb_op, k0, more, wave, rsa, rsb,
+                                        fa, fb, sn, an, bn);
   }
 }
 
@@ -348,11 +435,13 @@ __device__ __forceinline__ void last_substep(f32x16 (&acc)[4][4], const bf16x8 (
 // which immediately takes the DMAs of the stage after next.  The loop body
 // runs from ks1 of one stage to ks0 of the next, so the first MFMA group
 // (which starts from zero instead of the accumulators) sits before the loop.
-template <bool AT, bool BT, class Active>
+template <bool AT, bool BT, class Active, bool GATHER_A = false>
 __device__ __forceinline__ void gemm_tile_dma(const Operand& A, const Operand& B, int m0, int n0,
                                               int nsteps, Active active,
                                               f32x16 (&acc)[4][4], char* lds,
                                               L2Split sa = {0, 8}, L2Split sb = {0, 4}) {
+  static_assert(!GATHER_A || AT, "the gathered transposed loader is for a transposed A");
+  using LoaderA = std::conditional_t<GATHER_A, DmaTransposedGather, DmaLoader<AT>>;
   active.prepare(nsteps);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -371,7 +460,7 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand& A, const Operand& B
   }
   int nxt = active.next(cur + 1, nsteps);
 
-  DmaLoader<AT> la;
+  LoaderA la;
   DmaLoader<BT> lb;
   la.init(A, m0, wave, lane);
   lb.init(B, n0, wave, lane);
@@ -381,6 +470,7 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand& A, const Operand& B
   fb.init(wn * 128, lane);
   const uint32_t lbase = lds_addr(lds);
   auto issue = [&](int slot, int step) {
+    if constexpr (GATHER_A) la.rows(step * kDmaKStep);
     la.issue(lbase + slot * kDmaStageBytes, step * kDmaKStep, wave);
     lb.issue(lbase + slot * kDmaStageBytes + kDmaOpBytes, step * kDmaKStep, wave);
   };
@@ -425,6 +515,7 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand& A, const Operand& B
     mfma_group<false>(acc, a0, b0);
     interleave_reads_mfma<kReads>();
     const int nn = active.next(nxt + 1, nsteps);   // the stage after next
+    if constexpr (GATHER_A) la.rows((nn < nsteps ? nn : 0) * kDmaKStep);
     // own DMAs of the next stage; only the latest line touch may still fly
     // (loads complete in order, so every older one has landed too)
     wait_vmcnt<1>();
@@ -436,8 +527,10 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand& A, const Operand& B
       const int k0n = (more ? nn : 0) * kDmaKStep;
       const uint32_t la_op = lbase + slot * kDmaStageBytes;
       const char* sn = lds + (slot ^ 1) * kDmaStageBytes;
-      last_substep<0, AT, BT>(acc, a1, b1, la, lb, la_op, la_op + kDmaOpBytes, k0n, more, wave,
-                              la.rsrc(k0n), lb.rsrc(k0n), fa, fb, sn, a0, b0);
+      last_substep<0, AT, BT, LoaderA, DmaLoader<BT>>(acc, a1, b1, la, lb, la_op,
+                                                      la_op + kDmaOpBytes, k0n, more, wave,
+                                                      la.rsrc(k0n), lb.rsrc(k0n), fa, fb, sn, a0,
+                                                      b0);
     }
     prefetch(nn + 2);   // after the DMAs: the wait above leaves only this one in flight
     {

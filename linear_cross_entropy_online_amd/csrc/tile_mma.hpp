@@ -65,6 +65,13 @@ struct Operand {
   int64_t ld;        // elements between consecutive stored rows
   int64_t mext;      // M (natural: stored rows; transposed: stored columns) readable
   int64_t kext;      // K readable
+  // Optional (bf16 LDS-DMA core only), rows gathered through a map; byte
+  // offsets of mapped rows must stay below 2^31.
+  //  natural operand: stored row r (M) is row rowmap[r] of `base` (global map);
+  //  transposed operand: k row k is row table[k % 2][k / 2] of `base`, where
+  //  rowmap points at an LDS table with rowmap_half entries per parity.
+  const int* rowmap = nullptr;
+  int rowmap_half = 0;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* p) {

@@ -69,8 +69,16 @@ def test_invalid_dtype_reduction_flags_eps():
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_DTYPE
     d = L.make_desc(8, 64, 10, reduction=5)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
-    d = L.make_desc(8, 64, 10, flags=2)
+    d = L.make_desc(8, 64, 10, flags=4)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    # row compaction: bf16 only, and 32-bit byte offsets of gathered rows
+    import torch
+    d = L.make_desc(8, 64, 10, dtype=torch.float32, flags=_abi.FLCE_FLAG_COMPACT_IGNORED)
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    d = L.make_desc(1 << 18, 2048, 10, flags=_abi.FLCE_FLAG_COMPACT_IGNORED)
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    d = L.make_desc(131072, 2048, 151552, flags=_abi.FLCE_FLAG_COMPACT_IGNORED)
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_OK
     d = L.make_desc(8, 64, 10, filter_eps=-1.0)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
     d = L.make_desc(8, 64, 10, filter_eps=float("nan"))

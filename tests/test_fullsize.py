@@ -75,6 +75,39 @@ def test_large_vocab_full(large_vocab):
 
 
 @pytest.mark.timeout(900)
+def test_large_vocab_compacted(large_vocab):
+    """Ignored-row compaction at full size (the bench's launch with the flag):
+    kept rows against the oracle on samples, removed rows exactly zero."""
+    H, W, y, Hd, Wd, yd, lse_ref = large_vocab
+    loss, rows, lse, dH, dW = L.flce_fused_fwd_bwd(Hd, Wd, yd,
+                                                   flags=L.FLCE_FLAG_COMPACT_IGNORED)
+    torch.cuda.synchronize()
+    yn = y.numpy()
+    valid = yn != -100
+    idx = np.nonzero(valid)[0]
+    zy = np.zeros(len(yn))
+    zy[idx] = np.einsum("nd,nd->n", np64(H[idx]), np64(W[yn[idx]]))
+    rows_ref = np.where(valid, lse_ref - zy, 0.0)
+    g = O.row_scale(yn, W.shape[0], -100, "mean")
+    rs = _sample(H.shape[0], 48, 11)
+    vs = _sample(W.shape[0], 48, 12, extra=yn[idx[:8]].tolist())
+    dH_ref = O.dH_rows(H, W, y, lse_ref, g, rs)
+    dW_ref = O.dW_rows(H, W, y, lse_ref, g, vs)
+    lse_c = lse.cpu().numpy()
+    vals = dict(loss=rel(loss.item(), rows_ref.sum() / valid.sum()),
+                lse=max_abs_rel(lse_c[valid], lse_ref[valid]),
+                loss_rows=max_abs_rel(rows, rows_ref), dH=max_abs_rel(dH[rs], dH_ref),
+                dW=max_abs_rel(dW[vs], dW_ref))
+    report("large_vocab_compacted", **vals)
+    tol = TOL["bf16"]
+    assert vals["loss"] <= tol["loss"] and vals["lse"] <= tol["loss"]
+    assert vals["loss_rows"] <= tol["loss"]
+    assert vals["dH"] <= tol["grad"] and vals["dW"] <= tol["grad"]
+    assert np.all(lse_c[~valid] == 0)
+    _properties("large_vocab_compacted", H, W, y, dH.cpu(), dW.cpu())
+
+
+@pytest.mark.timeout(900)
 def test_large_vocab_filter(large_vocab):
     """Filter on at 2^-12: whole 64 x 64 blocks sampled against the filtered
     oracle; the error against the exact oracle is reported."""

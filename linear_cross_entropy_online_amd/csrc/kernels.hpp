@@ -768,6 +768,9 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
   if (is_h) {
     grouped_tile(local, Td, T3n, 4, td, tr);   // d tile, band row tile
     if (COMPACT && tr * kTile >= nrows) return;   // ignored rows only: zeroed separately
+    out = dH + (int64_t)band.nb0 * D;
+    rvalid = COMPACT ? nrows : band.ns_cur;
+    beta = beta_h;
     const Operand A{reinterpret_cast<const char*>(W + (int64_t)band.vb0 * D), D, D, band.vs_cur};
     const int kpad = (band.vs_cur + kTile - 1) / kTile * kTile;
     const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T3n * kTile, kpad};
@@ -775,13 +778,14 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
       const SkipRowsOfFlags<step_k<T>()> act{flagsT + tr * 4, band.frows};
       tile_contract<T, true, false>(A, B, td * kTile, tr * kTile, band.vs_cur, act, acc, lds);
     } else {
-      tile_contract<T, true, false>(A, B, td * kTile, tr * kTile, band.vs_cur, AllActive{}, acc, lds);
+      tile_contract<T, true, false>(A, B, td * kTile, tr * kTile, band.vs_cur, AllActive{}, acc,
+                                    lds);
     }
-    out = dH + (int64_t)band.nb0 * D;
-    rvalid = COMPACT ? nrows : band.ns_cur;
-    beta = beta_h;
   } else {
     grouped_tile(local, Td, T2n, 4, td, tr);   // d tile, band vocabulary tile
+    out = dW + (int64_t)band.vb0 * D;
+    rvalid = band.vs_cur;
+    beta = beta_w;
     const int K = nrows > 0 ? nrows : 0;
     if constexpr (COMPACT) {
       char* table = lds + kDmaLdsBytes + 256;
@@ -810,9 +814,6 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
                                      lds);
       }
     }
-    out = dW + (int64_t)band.vb0 * D;
-    rvalid = band.vs_cur;
-    beta = beta_w;
   }
   // acc[i][j][4q + e]: d = dw + 32 i + 8 q + 4 (lane / 32) + e, row = rw + 32 j + lane % 32.
   // Buffer accesses relative to the tile's first output row: an offset past
@@ -827,12 +828,12 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
       scatter ? dH : out + (int64_t)row0 * D));
   const int dw = td * kTile + wm * 128 + 4 * (lane >> 5);
   const int lw = wn * 128 + (lane & 31);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  // Two row groups in flight: the loads of group j + 1 (and j + 2) are out
+  // while group j is added and stored.
+  auto offsets = [&](int j, uint32_t (&off)[4][4]) {
     const int lr = lw + 32 * j;
     const bool rok = row0 + lr < rvalid;
     const int64_t orow = scatter ? (rok ? (int64_t)a.rowmap[band.nb0 + row0 + lr] : 0) : lr;
-    uint32_t off[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -840,7 +841,8 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
         const int d = dw + 32 * i + 8 * q;
         off[i][q] = rok && d < D ? (uint32_t)((orow * D + d) * 4) : kOob;
       }
-    f32x4 old[4][4];
+  };
+  auto load = [&](const uint32_t (&off)[4][4], f32x4 (&old)[4][4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -848,6 +850,8 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
         old[i][q] = beta ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                          rs, off[i][q], 0, 0))
                          : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto store = [&](int j, const uint32_t (&off)[4][4], const f32x4 (&old)[4][4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -856,7 +860,21 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
                               acc[i][j][4 * q + 3]} + old[i][q];
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off[i][q], 0, 0);
       }
-  }
+  };
+  uint32_t offA[4][4], offB[4][4];
+  f32x4 oldA[4][4], oldB[4][4];
+  offsets(0, offA);
+  load(offA, oldA);
+  offsets(1, offB);
+  load(offB, oldB);
+  store(0, offA, oldA);
+  offsets(2, offA);
+  load(offA, oldA);
+  store(1, offB, oldB);
+  offsets(3, offB);
+  load(offB, oldB);
+  store(2, offA, oldA);
+  store(3, offB, oldB);
 }
 
 // One launch of the backward pipeline: the gradient tiles of band k - 1

@@ -173,6 +173,8 @@ def parse():
     p.add_argument("--filter-eps", type=float, default=0.0)
     p.add_argument("--compact-ignored", action="store_true",
                    help="remove rows whose target is ignore_index before every contraction")
+    p.add_argument("--bf16-grads", action="store_true",
+                   help="dH and dW written in bf16 (FLCE_FLAG_BF16_GRADS)")
     p.add_argument("--cpu-rows", type=int, default=8192,
                    help="rows of the workload the oracle runs for cpu_baseline (0 = skip)")
     p.add_argument("--no-profile-pass", action="store_true")
@@ -190,16 +192,22 @@ def parse():
     return p.parse_args()
 
 
-def backward_flops_by_class(plan, N, D, V):
+def backward_flops_by_class(plan, N, D, V, serial=False):
     """Algorithmic flops of the backward launch classes, following the
     library's launch sequence: launch k holds the dZ tiles of band k
     (2 ns vs D) and the gradient tiles of band k - 1 (4 ns vs D); the first
-    launch is class bwd_dz, the last bwd_grad, the others bwd_band."""
+    launch is class bwd_dz, the last bwd_grad, the others bwd_band.  serial
+    (bf16 gradients): every band is a bwd_dz launch then a bwd_grad launch."""
     NS, VS, nbn, nbv = (plan["band_rows"], plan["band_vocab"], plan["n_bands_rows"],
                         plan["n_bands_vocab"])
     bands = [(max(0, min(NS, N - bn * NS)), min(VS, V - bv * VS)) for bn in range(nbn)
              for bv in range(nbv)]
     out = {"bwd_dz": 0.0, "bwd_grad": 0.0, "bwd_band": 0.0}
+    if serial:
+        for ns, vs in bands:
+            out["bwd_dz"] += 2.0 * ns * vs * D
+            out["bwd_grad"] += 4.0 * ns * vs * D
+        return out
     nb = len(bands)
     for k in range(nb + 1):
         cls = "bwd_dz" if k == 0 else ("bwd_grad" if k == nb else "bwd_band")
@@ -262,11 +270,14 @@ def main():
     Hd, Wd, yd = H.to(dev), W.to(dev), y.to(dev)
     N, D, V = wl.n, wl.d, wl.v
     flags0 = L.FLCE_FLAG_COMPACT_IGNORED if args.compact_ignored else 0
+    if args.bf16_grads:
+        flags0 |= L.FLCE_FLAG_BF16_GRADS
+    gdt = torch.bfloat16 if args.bf16_grads else torch.float32
     plan = L.flce_plan(N, D, V, dtype=Hd.dtype, reduction=wl.reduction,
                        filter_eps=args.filter_eps, flags=flags0)
     ws = L.Workspace(plan["ws_bytes"], dev)
     outs = (torch.empty(1, device=dev), torch.empty(N, device=dev), torch.empty(N, device=dev),
-            torch.empty(N, D, device=dev), torch.empty(V, D, device=dev))
+            torch.empty(N, D, device=dev, dtype=gdt), torch.empty(V, D, device=dev, dtype=gdt))
 
     def step(flags=0):
         L.flce_fused_fwd_bwd(Hd, Wd, yd, reduction=wl.reduction, filter_eps=args.filter_eps,
@@ -329,7 +340,7 @@ def main():
     n_bands = plan["n_bands_rows"] * plan["n_bands_vocab"]
     # with compaction the contractions cover only the kept rows
     n_eff = int((y != fi.IGNORE_INDEX).sum()) if args.compact_ignored else N
-    flops_per_step = backward_flops_by_class(plan, n_eff, D, V)
+    flops_per_step = backward_flops_by_class(plan, n_eff, D, V, serial=args.bf16_grads)
     flops_per_step["fwd_lse"] = 2.0 * n_eff * D * V
     roofline = None
     if kernels:
@@ -339,7 +350,7 @@ def main():
         achieved = per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
         traffic = None
         if (dom == "bwd_band" and args.workload == "large_vocab" and args.filter_eps == 0.0
-                and not args.compact_ignored):
+                and not args.compact_ignored and not args.bf16_grads):
             traffic = stored_traffic()
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                     "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -359,12 +370,14 @@ def main():
         "config": {"workload": wl.name, "N": N, "D": D, "V": V, "reduction": wl.reduction,
                    "ignore_frac": wl.ignore_frac, "filter_eps": args.filter_eps,
                    "compact_ignored": bool(args.compact_ignored),
+                   "grad_dtype": "bf16" if args.bf16_grads else "f32",
                    "parallelism": "single GPU"},
         "mfma_util": round(tflops / peak, 4), "tflops_counted_8ndv": round(tflops, 1),
         "ms_median": round(float(np.median(per)), 4), "ms_p95": round(float(np.percentile(per, 95)), 4),
         "peak_extra_mib": round(plan["ws_bytes"] / 2**20, 2),
         "torch_peak_alloc_delta_mib": round(peak_extra / 2**20, 2),
-        "total_mib_incl_outputs": round((plan["ws_bytes"] + 4 * (2 * N + 1 + N * D + V * D))
+        "total_mib_incl_outputs": round((plan["ws_bytes"] + 4 * (2 * N + 1)
+                                         + (2 if args.bf16_grads else 4) * (N * D + V * D))
                                         / 2**20, 1),
         "plan": {"band_rows": NS, "band_vocab": VS, "bands": n_bands,
                  "fwd_band_rows": plan["fwd_band_rows"], "fwd_workgroups": plan["fwd_workgroups"]},

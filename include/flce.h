@@ -24,8 +24,9 @@
  *     aligned).  Extra device memory of a call is therefore exactly ws_bytes.
  *   - Layouts are row-major and contiguous: H [N,D], W [V,D], dH [N,D],
  *     dW [V,D]; y is int64 [N]; loss_rows, lse are float [N]; loss is float [1].
- *     H and W share one element type (desc->in_dtype); gradients are float.
- *     H, W, dH, dW must be 16-byte aligned.
+ *     H and W share one element type (desc->in_dtype); gradients dH, dW are
+ *     float, or bf16 under FLCE_FLAG_BF16_GRADS.  H, W, dH, dW must be
+ *     16-byte aligned.
  *   - Work is enqueued on `stream` (0 = the null stream) and runs
  *     asynchronously; no entry point synchronises except
  *     flce_device_status().  Outputs are overwritten, never accumulated.
@@ -71,7 +72,7 @@ enum { FLCE_MEAN = 0, FLCE_SUM = 1, FLCE_NONE = 2 }; /* loss reduction          
 enum {
   FLCE_FLAG_PROFILE = 1u,          /* record HIP events around every launch (see
                                       flce_profile_read); costs a little time  */
-  FLCE_FLAG_COMPACT_IGNORED = 2u   /* remove the rows whose target is ignore_index
+  FLCE_FLAG_COMPACT_IGNORED = 2u,  /* remove the rows whose target is ignore_index
                                       before every contraction (CCE App. B):
                                       the tiles cover only the other rows.  Their
                                       loss_rows entry, dH row and dW contribution
@@ -80,6 +81,24 @@ enum {
                                       only, and N * D * 4 < 2^31; otherwise
                                       FLCE_E_UNSUPPORTED.  Adds N int32 and
                                       ceil(N/1024) int32 to the workspace.    */
+  FLCE_FLAG_BF16_GRADS = 4u        /* dH and dW are bf16 (the parameters' type)
+                                      instead of float: the gradient type a
+                                      bf16 training loop keeps (CCE Sec. 5.1 with
+                                      Table 1 rows 8-10 sums gradients in the
+                                      final type, Kahan optional;
+                                      p2 section "precision policy는 속도 옵션이
+                                      아니라 gradient 계약이다" makes the
+                                      accumulator a choice).  bf16 inputs only,
+                                      else FLCE_E_UNSUPPORTED.  Accumulation:
+                                      dH of a token band is summed over the
+                                      vocabulary bands in a float stage in the
+                                      workspace (NS x D floats) and rounded to
+                                      bf16 once; dW of a vocabulary band is
+                                      rounded once per token band
+                                      (n_bands_rows roundings to nearest even).
+                                      The backward then stages one dZ band and
+                                      runs each band as a dZ launch followed by
+                                      a gradient launch.                     */
 };
 
 typedef struct flce_desc {
@@ -109,7 +128,8 @@ typedef struct flce_plan_info {
   int32_t fwd_workgroups;  /* forward grid of one band (256 x 256 logits tiles) */
   int32_t tile;            /* output tile edge of every contraction (256)      */
   int32_t filter_block;    /* edge of a filter block (64)                      */
-  int64_t dz_bytes;        /* bytes of one of the two staged dZ band buffers   */
+  int64_t dz_bytes;        /* bytes of one staged dZ band buffer (two of them,
+                              or one with FLCE_FLAG_BF16_GRADS)                */
 } flce_plan_info;
 
 /* Exact workspace size for *d (the maximum over the three compute entry
@@ -130,7 +150,8 @@ int flce_forward(const flce_desc* d, const void* H, const void* W, const int64_t
                  float* loss_rows, float* lse, float* loss,
                  void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Backward: dH [N,D] and dW [V,D] (float, overwritten) from the forward's lse.
+/* Backward: dH [N,D] and dW [V,D] (float, or bf16 under FLCE_FLAG_BF16_GRADS;
+ * overwritten) from the forward's lse.
  * dloss is a device pointer: [1] for FLCE_MEAN / FLCE_SUM, [N] for FLCE_NONE;
  * NULL means an upstream gradient of 1.  The logits are recomputed block by
  * block, dZ is staged in ws one band at a time (bf16 for bf16 inputs, float
@@ -138,16 +159,17 @@ int flce_forward(const flce_desc* d, const void* H, const void* W, const int64_t
  * contracted) and contracted into dH and dW (CCE Alg. 4 structure). */
 int flce_backward(const flce_desc* d, const void* H, const void* W, const int64_t* y,
                   const float* lse, const float* dloss,
-                  float* dH, float* dW,
+                  void* dH, void* dW,
                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Forward then backward with an upstream gradient of 1, in one call. */
 int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const int64_t* y,
                        float* loss_rows, float* lse, float* loss,
-                       float* dH, float* dW,
+                       void* dH, void* dW,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Multiplies dH [N,D] and dW [V,D] (float, in place, 16-byte aligned) by the
+/* Multiplies dH [N,D] and dW [V,D] (in place, 16-byte aligned; float, or
+ * bf16 under FLCE_FLAG_BF16_GRADS, rounded to nearest even) by the
  * upstream gradient dloss[0] (device pointer; NULL means 1: nothing to do).
  * Together with flce_fused_fwd_bwd this is the contract in which the forward
  * already computes the gradients: p1 (Trillion Labs FLCE notes) section
@@ -158,7 +180,7 @@ int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const i
  * scalar.  reduction == FLCE_NONE returns FLCE_E_UNSUPPORTED: a per-row
  * upstream gradient cannot be applied after the contraction, so that path
  * recomputes (flce_backward).  No workspace is used. */
-int flce_scale_gradients(const flce_desc* d, const float* dloss, float* dH, float* dW,
+int flce_scale_gradients(const flce_desc* d, const float* dloss, void* dH, void* dW,
                          hipStream_t stream);
 
 /* Synchronises `stream`, then reads the status word of `ws` into *out
@@ -173,8 +195,10 @@ enum {
   FLCE_K_FWD_LSE = 0,     /* forward contraction + online max/sum-exp        */
   FLCE_K_LSE_COMBINE = 1, /* per-row merge of partials, loss rows            */
   FLCE_K_FINALIZE = 2,    /* scalar loss / row scale                         */
-  FLCE_K_BWD_DZ = 3,      /* first backward launch: dZ of band 0 only        */
-  FLCE_K_BWD_GRAD = 4,    /* last backward launch: dH, dW of the last band   */
+  FLCE_K_BWD_DZ = 3,      /* backward launches of dZ tiles only (the first
+                             one; every band's first under BF16_GRADS)        */
+  FLCE_K_BWD_GRAD = 4,    /* backward launches of dH, dW tiles only (the last
+                             one; every band's second under BF16_GRADS)      */
   FLCE_K_AUX = 5,         /* small fills                                     */
   FLCE_K_BWD_BAND = 6,    /* other backward launches: dH += dZ W_band and
                              dW_band (+)= dZ^T H_band of band k - 1 together

@@ -22,7 +22,8 @@ import ctypes
 import torch
 
 from . import _abi
-from ._abi import (FLCE_BF16, FLCE_F32, FLCE_FLAG_COMPACT_IGNORED, FLCE_FLAG_PROFILE, FLCE_K_AUX,
+from ._abi import (FLCE_BF16, FLCE_F32, FLCE_FLAG_BF16_GRADS, FLCE_FLAG_COMPACT_IGNORED,
+                   FLCE_FLAG_PROFILE, FLCE_K_AUX,
                    FLCE_K_BWD_BAND,
                    FLCE_K_BWD_DZ, FLCE_K_BWD_GRAD, FLCE_K_COUNT, FLCE_K_FINALIZE, FLCE_K_FWD_LSE,
                    FLCE_K_LSE_COMBINE, FLCE_MEAN, FLCE_NONE, FLCE_SUM, FlceError, lib)
@@ -30,7 +31,8 @@ from ._abi import (FLCE_BF16, FLCE_F32, FLCE_FLAG_COMPACT_IGNORED, FLCE_FLAG_PRO
 __all__ = ["flce_workspace_bytes", "flce_plan", "flce_forward", "flce_backward",
            "flce_fused_fwd_bwd", "flce_scale_gradients", "flce_device_status", "flce_profile_reset",
            "flce_profile_read", "linear_cross_entropy", "Workspace", "FlceError", "lib",
-           "FLCE_FLAG_PROFILE", "FLCE_FLAG_COMPACT_IGNORED", "KERNEL_CLASSES"]
+           "FLCE_FLAG_PROFILE", "FLCE_FLAG_COMPACT_IGNORED", "FLCE_FLAG_BF16_GRADS",
+           "KERNEL_CLASSES"]
 
 _RED = {"mean": FLCE_MEAN, "sum": FLCE_SUM, "none": FLCE_NONE}
 KERNEL_CLASSES = {"fwd_lse": FLCE_K_FWD_LSE, "lse_combine": FLCE_K_LSE_COMBINE,
@@ -138,10 +140,15 @@ def flce_forward(H, W, y, reduction="mean", ignore_index=-100, filter_eps=0.0, f
     return loss, loss_rows, lse
 
 
+def _grad_dtype(flags):
+    return torch.bfloat16 if flags & FLCE_FLAG_BF16_GRADS else torch.float32
+
+
 def flce_backward(H, W, y, lse, dloss=None, reduction="mean", ignore_index=-100, filter_eps=0.0,
                   flags=0, ws: Workspace | None = None, ws_budget_bytes=0, out=None):
-    """Returns (dH [N,D], dW [V,D]) float32.  dloss: device float32 [1] (mean/sum) or
-    [N] (none), or None for an upstream gradient of 1."""
+    """Returns (dH [N,D], dW [V,D]): float32, or bfloat16 with FLCE_FLAG_BF16_GRADS.
+    dloss: device float32 [1] (mean/sum) or [N] (none), or None for an upstream
+    gradient of 1."""
     _check_inputs(H, W, y)
     N, D = H.shape
     V = W.shape[0]
@@ -153,8 +160,8 @@ def flce_backward(H, W, y, lse, dloss=None, reduction="mean", ignore_index=-100,
         if dloss.numel() != need:
             raise FlceError(_abi.FLCE_E_SHAPE, f"dloss must have {need} elements")
     if out is None:
-        dH = torch.empty(N, D, dtype=torch.float32, device=H.device)
-        dW = torch.empty(V, D, dtype=torch.float32, device=H.device)
+        dH = torch.empty(N, D, dtype=_grad_dtype(flags), device=H.device)
+        dW = torch.empty(V, D, dtype=_grad_dtype(flags), device=H.device)
     else:
         dH, dW = out
     _abi.check(lib().flce_backward(ctypes.byref(d), _ptr(H), _ptr(W), _ptr(y), _ptr(lse),
@@ -177,8 +184,8 @@ def flce_fused_fwd_bwd(H, W, y, reduction="mean", ignore_index=-100, filter_eps=
         loss = None if reduction == "none" else torch.empty(1, dtype=torch.float32, device=dev)
         loss_rows = torch.empty(N, dtype=torch.float32, device=dev)
         lse = torch.empty(N, dtype=torch.float32, device=dev)
-        dH = torch.empty(N, D, dtype=torch.float32, device=dev)
-        dW = torch.empty(V, D, dtype=torch.float32, device=dev)
+        dH = torch.empty(N, D, dtype=_grad_dtype(flags), device=dev)
+        dW = torch.empty(V, D, dtype=_grad_dtype(flags), device=dev)
     else:
         loss, loss_rows, lse, dH, dW = out
     _abi.check(lib().flce_fused_fwd_bwd(ctypes.byref(d), _ptr(H), _ptr(W), _ptr(y),
@@ -190,10 +197,14 @@ def flce_fused_fwd_bwd(H, W, y, reduction="mean", ignore_index=-100, filter_eps=
 
 def flce_scale_gradients(dH, dW, dloss, reduction="mean", dtype=torch.bfloat16):
     """dH *= dloss[0], dW *= dloss[0] in place on the device (dloss: device float32
-    [1], or None for 1).  reduction "none" is rejected by the library."""
+    [1], or None for 1); float32 or bfloat16 gradients (both the same type).
+    reduction "none" is rejected by the library."""
     N, D = dH.shape
     V = dW.shape[0]
-    d = make_desc(N, D, V, dtype, reduction)
+    if dH.dtype != dW.dtype or dH.dtype not in (torch.float32, torch.bfloat16):
+        raise FlceError(_abi.FLCE_E_DTYPE, "dH and dW must both be float32 or both bfloat16")
+    flags = FLCE_FLAG_BF16_GRADS if dW.dtype == torch.bfloat16 else 0
+    d = make_desc(N, D, V, dtype, reduction, flags=flags)
     if dloss is not None:
         dloss = dloss.to(device=dW.device, dtype=torch.float32).reshape(-1).contiguous()
         if dloss.numel() != 1:
@@ -224,19 +235,19 @@ def flce_profile_read(kernel_class) -> tuple[int, float]:
 
 class _LinearCrossEntropy(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, H, W, y, reduction, ignore_index, filter_eps):
+    def forward(ctx, H, W, y, reduction, ignore_index, filter_eps, flags):
         loss, loss_rows, lse = flce_forward(H, W, y, reduction, ignore_index, filter_eps)
         ctx.save_for_backward(H, W, y, lse)
-        ctx.cfg = (reduction, ignore_index, filter_eps)
+        ctx.cfg = (reduction, ignore_index, filter_eps, flags)
         return loss_rows if reduction == "none" else loss.reshape(())
 
     @staticmethod
     def backward(ctx, g):
         H, W, y, lse = ctx.saved_tensors
-        reduction, ignore_index, filter_eps = ctx.cfg
+        reduction, ignore_index, filter_eps, flags = ctx.cfg
         dH, dW = flce_backward(H, W, y, lse, g.reshape(-1).float(), reduction, ignore_index,
-                               filter_eps)
-        return dH.to(H.dtype), dW.to(W.dtype), None, None, None, None
+                               filter_eps, flags)
+        return dH.to(H.dtype), dW.to(W.dtype), None, None, None, None, None
 
 
 class _LinearCrossEntropyGradsInForward(torch.autograd.Function):
@@ -246,8 +257,9 @@ class _LinearCrossEntropyGradsInForward(torch.autograd.Function):
     section "scalar reduction에서는 forward가 gradient까지 계산한다").  The
     kept gradients are consumed by the first backward: a second one raises."""
     @staticmethod
-    def forward(ctx, H, W, y, reduction, ignore_index, filter_eps):
-        loss, _, _, dH, dW = flce_fused_fwd_bwd(H, W, y, reduction, ignore_index, filter_eps)
+    def forward(ctx, H, W, y, reduction, ignore_index, filter_eps, flags):
+        loss, _, _, dH, dW = flce_fused_fwd_bwd(H, W, y, reduction, ignore_index, filter_eps,
+                                                flags)
         ctx.grads = (dH, dW)
         ctx.dtypes = (H.dtype, W.dtype, reduction)
         return loss.reshape(())
@@ -261,20 +273,28 @@ class _LinearCrossEntropyGradsInForward(torch.autograd.Function):
         ctx.grads = None
         h_dtype, w_dtype, reduction = ctx.dtypes
         flce_scale_gradients(dH, dW, g.reshape(1).float(), reduction, h_dtype)
-        return dH.to(h_dtype), dW.to(w_dtype), None, None, None, None
+        return dH.to(h_dtype), dW.to(w_dtype), None, None, None, None, None
 
 
 def linear_cross_entropy(H, W, y, reduction="mean", ignore_index=-100, filter_eps=0.0,
-                         grads_in_forward=False):
+                         grads_in_forward=False, bf16_grads=False):
     """loss = CE(H W^T, y) without materialising the logits (autograd-aware).
 
     grads_in_forward: for mean / sum, do all the contraction work (forward,
     recompute and gradients) inside the forward and only scale dH and dW by the
-    upstream scalar in the backward; dH and dW (fp32) are held from forward to
+    upstream scalar in the backward; dH and dW are held from forward to
     backward, and only one backward is allowed.  reduction "none" always
-    recomputes in the backward."""
+    recomputes in the backward.
+
+    bf16_grads (bf16 inputs): the library writes dH and dW in bf16 directly
+    (FLCE_FLAG_BF16_GRADS) instead of float32 that is then cast, so no float
+    [V, D] gradient is ever allocated; dW takes one rounding per token band of
+    the backward plan instead of one."""
+    flags = FLCE_FLAG_BF16_GRADS if bf16_grads else 0
+    if bf16_grads and H.dtype != torch.bfloat16:
+        raise FlceError(_abi.FLCE_E_UNSUPPORTED, "bf16_grads needs bfloat16 inputs")
     if grads_in_forward and reduction != "none":
         return _LinearCrossEntropyGradsInForward.apply(H, W, y, reduction, ignore_index,
-                                                       filter_eps)
-    return _LinearCrossEntropy.apply(H, W, y, reduction, ignore_index, filter_eps)
+                                                       filter_eps, flags)
+    return _LinearCrossEntropy.apply(H, W, y, reduction, ignore_index, filter_eps, flags)
 

@@ -12,6 +12,8 @@
 //                        ceil(VS/256) for dW^T, reading dZ buffer (k-1) % 2)
 //                        and the dZ tiles of band k (ceil(VS/256) x
 //                        ceil(NS/256), writing buffer k % 2); nb + 1 launches
+//     (bf16 gradients: one dZ buffer, and per band a dZ launch then a
+//     gradient launch; dH of the token band summed in a float stage)
 // dH of a token band accumulates over the vocabulary bands and dW of a
 // vocabulary band over the token bands; the first contribution stores, the
 // rest add, all in stream order, so the result is deterministic.
@@ -49,7 +51,9 @@ struct Plan {
   size_t dz_bytes;     // one dZ band buffer
   size_t flag_bytes;   // one flag grid
   bool compact;        // ignored rows compacted away (row map in the workspace)
+  bool bf16g;          // bf16 gradients: one dZ buffer + a float dH stage
   int ncblk;           // compaction blocks
+  size_t stage_bytes;  // the dH stage of one token band (bf16 gradients)
   size_t off_rowmap, off_cblk;
   size_t off_zy, off_bsum, off_bcnt, off_flags, off_flagsT, off_big, total;
 };
@@ -61,7 +65,9 @@ int validate(const flce_desc* d) {
   if (d->hidden < 8 || d->hidden % 8 != 0 || d->hidden >= (int64_t(1) << 20)) return FLCE_E_SHAPE;
   if (d->in_dtype != FLCE_BF16 && d->in_dtype != FLCE_F32) return FLCE_E_DTYPE;
   if (d->reduction < FLCE_MEAN || d->reduction > FLCE_NONE) return FLCE_E_UNSUPPORTED;
-  if (d->flags & ~uint32_t(FLCE_FLAG_PROFILE | FLCE_FLAG_COMPACT_IGNORED)) return FLCE_E_UNSUPPORTED;
+  if (d->flags & ~uint32_t(FLCE_FLAG_PROFILE | FLCE_FLAG_COMPACT_IGNORED | FLCE_FLAG_BF16_GRADS))
+    return FLCE_E_UNSUPPORTED;
+  if ((d->flags & FLCE_FLAG_BF16_GRADS) && d->in_dtype != FLCE_BF16) return FLCE_E_UNSUPPORTED;
   if (d->flags & FLCE_FLAG_COMPACT_IGNORED) {
     // bf16 core only; gathered H rows and scattered dH rows use 32-bit byte offsets
     if (d->in_dtype != FLCE_BF16) return FLCE_E_UNSUPPORTED;
@@ -75,7 +81,22 @@ int validate(const flce_desc* d) {
 // flagsT x 2 | big, where `big` holds either the forward partials of one band
 // (2 x Tv x NF floats) or two backward dZ band buffers (NS x VS elements
 // each; one is written while the other is contracted): the forward's
-// partials are consumed before the first dZ band is written.
+// partials are consumed before the first dZ band is written.  With bf16
+// gradients the backward part of `big` is one dZ buffer and the float dH
+// stage of a token band (NS x D).
+size_t backward_bytes(const Plan& p) {
+  return p.bf16g ? p.dz_bytes + p.stage_bytes : 2 * p.dz_bytes;
+}
+
+// Forward band rows: as many as the backward part of `big` holds partials
+// for (2 Tv floats per row), a multiple of 256, at least 256.
+int forward_rows(const Plan& p, int64_t Npad) {
+  const size_t dz = size_t(p.NS) * p.VS * p.es;
+  const size_t bytes = p.bf16g ? dz + size_t(p.NS) * p.D * 4 : 2 * dz;
+  const int64_t fit = int64_t(bytes / (size_t(8) * p.Tv)) / 256 * 256;
+  return int(std::max<int64_t>(256, std::min<int64_t>(Npad, fit)));
+}
+
 size_t layout(Plan& p) {
   size_t o = 256;  // Header
   const size_t N = size_t(p.N);
@@ -99,7 +120,8 @@ size_t layout(Plan& p) {
   }
   p.off_big = o;
   p.dz_bytes = align256(size_t(p.NS) * p.VS * p.es);
-  p.big = std::max(2 * p.dz_bytes, size_t(2) * p.Tv * p.NF * 4);
+  p.stage_bytes = p.bf16g ? align256(size_t(p.NS) * p.D * 4) : 0;
+  p.big = std::max(backward_bytes(p), size_t(2) * p.Tv * p.NF * 4);
   o = align256(o + p.big);
   p.total = o;
   return o;
@@ -123,6 +145,7 @@ int make_plan(const flce_desc* d, Plan& p) {
   p.dtype = d->in_dtype;
   p.es = d->in_dtype == FLCE_BF16 ? 2 : 4;
   p.compact = (d->flags & FLCE_FLAG_COMPACT_IGNORED) != 0;
+  p.bf16g = (d->flags & FLCE_FLAG_BF16_GRADS) != 0;
   p.ncblk = int(cdiv(std::max<int64_t>(p.N, 1), flce::kCompactRows));
   p.Tv = int(cdiv(p.V, flce::kTile));
   const int64_t Npad = cdiv(std::max<int64_t>(p.N, 1), 256) * 256;
@@ -139,9 +162,7 @@ int make_plan(const flce_desc* d, Plan& p) {
     p.VS = vs;
     p.frows = p.NS / kFilterBlock;
     p.fcols = p.VS / kFilterBlock;
-    // forward band: as many token rows as fit in the dZ buffers' bytes (>= 256)
-    const int64_t fit = int64_t(size_t(p.NS) * p.VS * p.es / (size_t(4) * p.Tv)) / 256 * 256;
-    p.NF = int(std::max<int64_t>(256, std::min<int64_t>(Npad, fit)));
+    p.NF = forward_rows(p, Npad);
     return layout(p) <= budget;
   };
   int ns_best = 0, vs_best = 0;
@@ -164,10 +185,7 @@ int make_plan(const flce_desc* d, Plan& p) {
   p.VS = int(even_split(p.V, p.VS));
   p.frows = p.NS / kFilterBlock;
   p.fcols = p.VS / kFilterBlock;
-  {
-    const int64_t fit = int64_t(size_t(p.NS) * p.VS * p.es / (size_t(4) * p.Tv)) / 256 * 256;
-    p.NF = int(std::max<int64_t>(256, std::min<int64_t>(Npad, fit)));
-  }
+  p.NF = forward_rows(p, Npad);
   layout(p);
   p.nbf = int(cdiv(std::max<int64_t>(p.N, 1), p.NF));
   p.nbn = int(cdiv(std::max<int64_t>(p.N, 1), p.NS));
@@ -216,7 +234,8 @@ struct Ws {
   double* bsum;
   int* bcnt;
   uint8_t *flags[2], *flagsT[2];
-  char* dz[2];
+  char* dz[2];    // the same buffer twice with bf16 gradients
+  float* stage;  // dH stage of a token band (bf16 gradients)
   int* rowmap;   // null without compaction
   int* cblk;
 };
@@ -234,8 +253,9 @@ Ws carve(const Plan& p, void* ws) {
   for (int k = 0; k < 2; ++k) {
     w.flags[k] = reinterpret_cast<uint8_t*>(b + p.off_flags + k * p.flag_bytes);
     w.flagsT[k] = reinterpret_cast<uint8_t*>(b + p.off_flagsT + k * p.flag_bytes);
-    w.dz[k] = b + p.off_big + k * p.dz_bytes;
+    w.dz[k] = b + p.off_big + (p.bf16g ? 0 : k * p.dz_bytes);
   }
+  w.stage = p.bf16g ? reinterpret_cast<float*>(b + p.off_big + p.dz_bytes) : nullptr;
   return w;
 }
 
@@ -297,69 +317,114 @@ flce::BandArgs band_args(const Plan& p, int k) {
   return band;
 }
 
+// One backward launch: grid = g_grad gradient tiles (the first g_long of the
+// contraction with the longer K) + the dZ tiles of `da`.
+template <typename T, bool BF16G>
+void band_kernel(bool filt, bool compact, dim3 grid, hipStream_t s, const flce::GradArgs<T>& ga,
+                 const flce::DzArgs<T>& da, int g_long, int g_grad, int h_first) {
+  const dim3 block(flce::kThreads);
+  if constexpr (sizeof(T) == 2) {
+    if (compact) {
+      if (filt)
+        flce::bwd_band_kernel<T, true, true, BF16G><<<grid, block, 0, s>>>(ga, da, g_long, g_grad,
+                                                                           h_first);
+      else
+        flce::bwd_band_kernel<T, false, true, BF16G><<<grid, block, 0, s>>>(ga, da, g_long, g_grad,
+                                                                            h_first);
+      return;
+    }
+  }
+  if (filt)
+    flce::bwd_band_kernel<T, true, false, BF16G><<<grid, block, 0, s>>>(ga, da, g_long, g_grad,
+                                                                        h_first);
+  else
+    flce::bwd_band_kernel<T, false, false, BF16G><<<grid, block, 0, s>>>(ga, da, g_long, g_grad,
+                                                                         h_first);
+}
+
 // Bands k = 0 .. nb-1 (token-row band outer, vocabulary band inner).  Launch
 // k runs the gradient tiles of band k - 1 and the dZ tiles of band k, with
 // band k's dZ in buffer k % 2: the first launch only makes dZ, the last only
 // contracts.  Launches on one stream run in order, so band k - 1's dZ is
 // complete before its gradient tiles start, and buffer k % 2 is no longer
 // read (band k - 2's gradients ran in launch k - 1) when band k writes it.
+// bf16 gradients: one dZ buffer, and band k is a dZ launch followed by its
+// gradient launch; dH of a token band goes through the float stage (stored at
+// its first vocabulary band, added to at the middle ones, added, rounded and
+// written to dH at the last), dW is rounded once per token band.
 template <typename T>
 int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, const int64_t* y,
-              const float* lse, const float* dloss_rows, float* dH, float* dW, const Ws& w,
+              const float* lse, const float* dloss_rows, void* dH, void* dW, const Ws& w,
               bool prof, hipStream_t s) {
   const int N = int(p.N), D = int(p.D), V = int(p.V);
   const int Td = int(cdiv(D, flce::kTile));
   const int nb = p.nbn * p.nbv;
+  const bool filt = d->filter_eps > 0.f;
   if (w.rowmap)   // dH rows of ignored rows: no tile writes them
     FLCE_TRY(launch(FLCE_K_AUX, prof, s, [&] {
-      flce::zero_ignored_rows_kernel<<<dim3(int(cdiv(N, 16))), dim3(256), 0, s>>>(w.rowmap, w.hdr,
-                                                                                N, D, dH);
+      flce::zero_ignored_rows_kernel<<<dim3(int(cdiv(N, 16))), dim3(256), 0, s>>>(
+          w.rowmap, w.hdr, N, D * (p.bf16g ? 2 : 4), static_cast<char*>(dH));
     }));
+  auto dz_args = [&](int k, int buf) {
+    const flce::BandArgs band = band_args(p, k);
+    const int TMv = int(cdiv(band.vs_cur, flce::kTile));
+    const int TNn = int(cdiv(band.ns_cur, flce::kTile));
+    return flce::DzArgs<T>{static_cast<const T*>(H), static_cast<const T*>(W), y, lse, dloss_rows,
+                           w.hdr, N, D, V, d->ignore_index, d->reduction, d->filter_eps, band,
+                           TMv, TNn, reinterpret_cast<T*>(w.dz[buf]), w.flags[buf],
+                           w.flagsT[buf], w.rowmap};
+  };
+  // gradient tiles of band k reading buffer `buf`; g_long, g_grad, h_first out
+  auto grad_args = [&](int k, int buf, int& g_long, int& g_grad, int& h_first) {
+    const flce::BandArgs band = band_args(p, k);
+    const int T2n = int(cdiv(band.vs_cur, flce::kTile));
+    const int T3n = int(cdiv(band.ns_cur, flce::kTile));
+    const int bn = k / p.nbv, bv = k % p.nbv;
+    const int h_mode = p.nbv == 1 ? 3 : (bv == 0 ? 0 : (bv == p.nbv - 1 ? 2 : 1));
+    // the contraction with the longer K (dH^T: band vocabulary, dW^T: band rows) first
+    h_first = band.vs_cur >= band.ns_cur ? 1 : 0;
+    g_long = Td * (h_first ? T3n : T2n);
+    g_grad = Td * (T3n + T2n);
+    return flce::GradArgs<T>{static_cast<const T*>(H), static_cast<const T*>(W),
+                             reinterpret_cast<const T*>(w.dz[buf]), w.flags[buf], w.flagsT[buf],
+                             p.bf16g ? nullptr : static_cast<float*>(dH),
+                             p.bf16g ? nullptr : static_cast<float*>(dW), N, D, V, band, T3n, T2n,
+                             Td, bv > 0 ? 1 : 0, bn > 0 ? 1 : 0, w.rowmap, w.hdr,
+                             p.bf16g ? static_cast<uint16_t*>(dH) : nullptr,
+                             p.bf16g ? static_cast<uint16_t*>(dW) : nullptr, w.stage, h_mode};
+  };
+  if (p.bf16g) {
+    if constexpr (sizeof(T) == 2) {
+      for (int k = 0; k < nb; ++k) {
+        const flce::DzArgs<T> da = dz_args(k, 0);
+        FLCE_TRY(launch(FLCE_K_BWD_DZ, prof, s, [&] {
+          band_kernel<T, true>(filt, p.compact, dim3(da.TMv * da.TNn), s, flce::GradArgs<T>{}, da,
+                               0, 0, 1);
+        }));
+        int g_long = 0, g_grad = 0, h_first = 1;
+        const flce::GradArgs<T> ga = grad_args(k, 0, g_long, g_grad, h_first);
+        FLCE_TRY(launch(FLCE_K_BWD_GRAD, prof, s, [&] {
+          band_kernel<T, true>(filt, p.compact, dim3(g_grad), s, ga, flce::DzArgs<T>{}, g_long,
+                               g_grad, h_first);
+        }));
+      }
+      return FLCE_OK;
+    }
+    return FLCE_E_UNSUPPORTED;   // bf16 gradients need bf16 inputs (validated)
+  }
   for (int k = 0; k <= nb; ++k) {
     flce::DzArgs<T> da{};
     flce::GradArgs<T> ga{};
     int g_long = 0, g_grad = 0, g_dz = 0, h_first = 1;
     if (k < nb) {
-      const flce::BandArgs band = band_args(p, k);
-      const int TMv = int(cdiv(band.vs_cur, flce::kTile));
-      const int TNn = int(cdiv(band.ns_cur, flce::kTile));
-      da = flce::DzArgs<T>{static_cast<const T*>(H), static_cast<const T*>(W), y, lse, dloss_rows,
-                           w.hdr, N, D, V, d->ignore_index, d->reduction, d->filter_eps, band,
-                           TMv, TNn, reinterpret_cast<T*>(w.dz[k & 1]), w.flags[k & 1],
-                           w.flagsT[k & 1], w.rowmap};
-      g_dz = TMv * TNn;
+      da = dz_args(k, k & 1);
+      g_dz = da.TMv * da.TNn;
     }
-    if (k > 0) {
-      const flce::BandArgs band = band_args(p, k - 1);
-      const int T2n = int(cdiv(band.vs_cur, flce::kTile));
-      const int T3n = int(cdiv(band.ns_cur, flce::kTile));
-      const int bn = (k - 1) / p.nbv, bv = (k - 1) % p.nbv;
-      ga = flce::GradArgs<T>{static_cast<const T*>(H), static_cast<const T*>(W),
-                             reinterpret_cast<const T*>(w.dz[(k - 1) & 1]), w.flags[(k - 1) & 1],
-                             w.flagsT[(k - 1) & 1], dH, dW, N, D, V, band, T3n, T2n, Td,
-                             bv > 0 ? 1 : 0, bn > 0 ? 1 : 0, w.rowmap, w.hdr};
-      // the contraction with the longer K (dH^T: band vocabulary, dW^T: band rows) first
-      h_first = band.vs_cur >= band.ns_cur ? 1 : 0;
-      g_long = Td * (h_first ? T3n : T2n);
-      g_grad = Td * (T3n + T2n);
-    }
+    if (k > 0) ga = grad_args(k - 1, (k - 1) & 1, g_long, g_grad, h_first);
     const int cls = k == 0 ? FLCE_K_BWD_DZ : (k == nb ? FLCE_K_BWD_GRAD : FLCE_K_BWD_BAND);
     FLCE_TRY(launch(cls, prof, s, [&] {
-      const dim3 grid(g_grad + g_dz), block(flce::kThreads);
-      const bool filt = d->filter_eps > 0.f;
-      if constexpr (sizeof(T) == 2) {
-        if (w.rowmap) {
-          if (filt)
-            flce::bwd_band_kernel<T, true, true><<<grid, block, 0, s>>>(ga, da, g_long, g_grad, h_first);
-          else
-            flce::bwd_band_kernel<T, false, true><<<grid, block, 0, s>>>(ga, da, g_long, g_grad, h_first);
-          return;
-        }
-      }
-      if (filt)
-        flce::bwd_band_kernel<T, true, false><<<grid, block, 0, s>>>(ga, da, g_long, g_grad, h_first);
-      else
-        flce::bwd_band_kernel<T, false, false><<<grid, block, 0, s>>>(ga, da, g_long, g_grad, h_first);
+      band_kernel<T, false>(filt, p.compact, dim3(g_grad + g_dz), s, ga, da, g_long, g_grad,
+                            h_first);
     }));
   }
   return FLCE_OK;
@@ -379,9 +444,11 @@ int check_inputs(const Plan& p, const void* H, const void* W, const int64_t* y) 
   return FLCE_OK;
 }
 
-int zero_dW(const Plan& p, float* dW, bool prof, hipStream_t s) {
+// dW <- 0 (float or bf16: zero bits either way)
+int zero_dW(const Plan& p, void* dW, bool prof, hipStream_t s) {
   return launch(FLCE_K_AUX, prof, s, [&] {
-    flce::fill_f32_kernel<<<dim3(1024), dim3(256), 0, s>>>(dW, p.V * p.D, 0.f);
+    flce::fill_f32_kernel<<<dim3(1024), dim3(256), 0, s>>>(static_cast<float*>(dW),
+                                                           p.V * p.D / (p.bf16g ? 2 : 1), 0.f);
   });
 }
 
@@ -408,7 +475,7 @@ int flce_plan(const flce_desc* d, flce_plan_info* out) {
   out->fwd_workgroups = p.Tv * int(cdiv(std::min<int64_t>(p.NF, std::max<int64_t>(p.N, 1)), 256));
   out->tile = flce::kTile;
   out->filter_block = kFilterBlock;
-  out->dz_bytes = int64_t(p.NS) * p.VS * p.es;   // one of the two dZ buffers
+  out->dz_bytes = int64_t(p.NS) * p.VS * p.es;   // one dZ buffer
   return FLCE_OK;
 }
 
@@ -435,7 +502,7 @@ int flce_forward(const flce_desc* d, const void* H, const void* W, const int64_t
 }
 
 int flce_backward(const flce_desc* d, const void* H, const void* W, const int64_t* y,
-                  const float* lse, const float* dloss, float* dH, float* dW, void* ws,
+                  const float* lse, const float* dloss, void* dH, void* dW, void* ws,
                   size_t ws_bytes, hipStream_t stream) {
   Plan p;
   FLCE_TRY(make_plan(d, p));
@@ -463,7 +530,7 @@ int flce_backward(const flce_desc* d, const void* H, const void* W, const int64_
 }
 
 int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const int64_t* y,
-                       float* loss_rows, float* lse, float* loss, float* dH, float* dW, void* ws,
+                       float* loss_rows, float* lse, float* loss, void* dH, void* dW, void* ws,
                        size_t ws_bytes, hipStream_t stream) {
   Plan p;
   FLCE_TRY(make_plan(d, p));
@@ -490,7 +557,7 @@ int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const i
   return run_bands<float>(d, p, H, W, y, lse, nullptr, dH, dW, w, prof, stream);
 }
 
-int flce_scale_gradients(const flce_desc* d, const float* dloss, float* dH, float* dW,
+int flce_scale_gradients(const flce_desc* d, const float* dloss, void* dH, void* dW,
                          hipStream_t stream) {
   Plan p;
   FLCE_TRY(make_plan(d, p));
@@ -500,13 +567,18 @@ int flce_scale_gradients(const flce_desc* d, const float* dloss, float* dH, floa
     return FLCE_E_ALIGN;
   if (!dloss) return FLCE_OK;   // an upstream gradient of 1
   const bool prof = d->flags & FLCE_FLAG_PROFILE;
-  if (p.N > 0)
-    FLCE_TRY(launch(FLCE_K_AUX, prof, stream, [&] {
-      flce::scale_f32_kernel<<<dim3(2048), dim3(256), 0, stream>>>(dH, p.N * p.D, dloss);
-    }));
-  return launch(FLCE_K_AUX, prof, stream, [&] {
-    flce::scale_f32_kernel<<<dim3(2048), dim3(256), 0, stream>>>(dW, p.V * p.D, dloss);
-  });
+  auto scale = [&](void* g, int64_t n) {
+    return launch(FLCE_K_AUX, prof, stream, [&] {
+      if (p.bf16g)
+        flce::scale_bf16_kernel<<<dim3(2048), dim3(256), 0, stream>>>(static_cast<uint16_t*>(g), n,
+                                                                      dloss);
+      else
+        flce::scale_f32_kernel<<<dim3(2048), dim3(256), 0, stream>>>(static_cast<float*>(g), n,
+                                                                     dloss);
+    });
+  };
+  if (p.N > 0) FLCE_TRY(scale(dH, p.N * p.D));
+  return scale(dW, p.V * p.D);
 }
 
 int flce_device_status(const void* ws, hipStream_t stream, int32_t* out) {

@@ -431,15 +431,16 @@ compact_scatter_kernel(const int64_t* __restrict__ y, int N, int64_t ignore,
   }
 }
 
-// dH rows of the ignored rows (positions nvalid .. N of rowmap) <- 0
+// dH rows of the ignored rows (positions nvalid .. N of rowmap) <- 0; a row
+// is row_bytes long (a multiple of 16: D % 8 == 0).
 __global__ void __launch_bounds__(256)
 zero_ignored_rows_kernel(const int* __restrict__ rowmap, const Header* __restrict__ hdr, int N,
-                         int D, float* __restrict__ dH) {
+                         int row_bytes, char* __restrict__ dH) {
   const int c0 = blockIdx.x * 16;
   const int nval = hdr->nvalid;
   for (int c = c0 > nval ? c0 : nval; c < c0 + 16 && c < N; ++c) {
-    f32x4* row = reinterpret_cast<f32x4*>(dH + (int64_t)rowmap[c] * D);
-    for (int i = threadIdx.x; i < D / 4; i += 256) row[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4* row = reinterpret_cast<u32x4*>(dH + (int64_t)rowmap[c] * row_bytes);
+    for (int i = threadIdx.x; i < row_bytes / 16; i += 256) row[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -459,6 +460,24 @@ __global__ void scale_f32_kernel(float* __restrict__ p, int64_t n, const float* 
     p4[i] = p4[i] * g;
   for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
     p[i] *= g;
+}
+
+// The same for bf16 values: p[i] = bf16(p[i] * s[0]) (round to nearest even),
+// n a multiple of 8, p 16-byte aligned.
+__global__ void scale_bf16_kernel(uint16_t* __restrict__ p, int64_t n, const float* __restrict__ s) {
+  const float g = s[0];
+  const int64_t n8 = n >> 3;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  u32x4* __restrict__ p8 = reinterpret_cast<u32x4*>(p);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const u32x4 v = p8[i];
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = pack_bf16x2(__builtin_bit_cast(float, v[e] << 16) * g,
+                         __builtin_bit_cast(float, v[e] & 0xffff0000u) * g);
+    p8[i] = o;
+  }
 }
 
 __global__ void clear_status_kernel(Header* __restrict__ hdr, float* __restrict__ loss) {
@@ -738,7 +757,95 @@ struct GradArgs {
   int beta_h, beta_w;      // accumulate into dH / dW (else overwrite)
   const int* rowmap;       // row compaction (COMPACT): band rows are positions of rowmap
   const Header* hdr;       // nvalid with row compaction
+  // bf16 gradients (BF16G): dH, dW are bf16; dH of the token band is summed in
+  // `stage` [NS][D] floats.  h_mode: 0 stage = acc, 1 stage += acc,
+  // 2 dH = bf16(stage + acc), 3 dH = bf16(acc); dW = bf16(acc) or, with beta_w,
+  // bf16(dW + acc).
+  uint16_t* dHb;
+  uint16_t* dWb;
+  float* stage;
+  int h_mode;
 };
+
+// Epilogue of a gradient tile with bf16 in or out: out[r][d] = acc + src[r][d]
+// (src optional) for the tile rows r < rvalid - row0 and d < D.  src rows are
+// the tile's rows; out rows are the same or, with `map`, map[r].  Same
+// two-row-groups-in-flight order as the float epilogue; bf16 values are
+// widened exactly and rounded to nearest even once.
+template <bool SRC_BF16, bool DST_BF16>
+__device__ __forceinline__ void grad_epilogue_cvt(const f32x16 (&acc)[4][4], bool src_on,
+                                                  __amdgpu_buffer_rsrc_t rsS,
+                                                  __amdgpu_buffer_rsrc_t rsD, const int* map,
+                                                  int row0, int rvalid, int D, int dw, int lw) {
+  constexpr int SES = SRC_BF16 ? 2 : 4, DES = DST_BF16 ? 2 : 4;
+  auto offsets = [&](int j, uint32_t (&os)[4][4], uint32_t (&od)[4][4]) {
+    const int lr = lw + 32 * j;
+    const bool rok = row0 + lr < rvalid;
+    const int64_t orow = map ? (rok ? (int64_t)map[lr] : 0) : lr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = dw + 32 * i + 8 * q;
+        const bool ok = rok && d < D;
+        os[i][q] = ok ? (uint32_t)(((int64_t)lr * D + d) * SES) : kOob;
+        od[i][q] = ok ? (uint32_t)((orow * D + d) * DES) : kOob;
+      }
+  };
+  auto load = [&](const uint32_t (&os)[4][4], u32x4 (&old)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (SRC_BF16) {
+          const u32x2 v = src_on ? __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                                 rsS, os[i][q], 0, 0))
+                                 : u32x2{0u, 0u};
+          old[i][q] = u32x4{v[0], v[1], 0u, 0u};
+        } else {
+          old[i][q] = src_on ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                             rsS, os[i][q], 0, 0))
+                             : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+  };
+  auto store = [&](int j, const uint32_t (&od)[4][4], const u32x4 (&old)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 o;
+        if constexpr (SRC_BF16)   // element d in the low half of a dword
+          o = f32x4{__builtin_bit_cast(float, old[i][q][0] << 16),
+                    __builtin_bit_cast(float, old[i][q][0] & 0xffff0000u),
+                    __builtin_bit_cast(float, old[i][q][1] << 16),
+                    __builtin_bit_cast(float, old[i][q][1] & 0xffff0000u)};
+        else
+          o = __builtin_bit_cast(f32x4, old[i][q]);
+        const f32x4 v = f32x4{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                              acc[i][j][4 * q + 3]} + o;
+        if constexpr (DST_BF16)
+          __builtin_amdgcn_raw_buffer_store_b64(
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rsD, od[i][q], 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsD, od[i][q], 0, 0);
+      }
+  };
+  uint32_t sA[4][4], dA[4][4], sB[4][4], dB[4][4];
+  u32x4 oldA[4][4], oldB[4][4];
+  offsets(0, sA, dA);
+  load(sA, oldA);
+  offsets(1, sB, dB);
+  load(sB, oldB);
+  store(0, dA, oldA);
+  offsets(2, sA, dA);
+  load(sA, oldA);
+  store(1, dB, oldB);
+  offsets(3, sB, dB);
+  load(sB, oldB);
+  store(2, dA, oldA);
+  store(3, dB, oldB);
+}
 
 // Gradient tile `local` of one of the band's two contractions (is_h: dH^T).
 // COMPACT: the band's rows are positions of a.rowmap; only the first
@@ -746,7 +853,7 @@ struct GradArgs {
 // not made): dH^T tiles past them exit, their rows are scattered through the
 // map, and dW^T contracts over them only, gathering H's rows through an LDS
 // copy of the map.
-template <typename T, bool FILTER, bool COMPACT = false>
+template <typename T, bool FILTER, bool COMPACT = false, bool BF16G = false>
 __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int local, char* lds) {
   const T* __restrict__ H = a.H;
   const T* __restrict__ W = a.W;
@@ -821,13 +928,34 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
   // the 16 loads of a row group go out together, with no branches between
   // them.
   const int row0 = tr * kTile;
+  const int dw = td * kTile + wm * 128 + 4 * (lane >> 5);
+  const int lw = wn * 128 + (lane & 31);
+  if constexpr (BF16G) {
+    if (is_h) {
+      const int hm = a.h_mode;
+      const auto rsS = make_rsrc(reinterpret_cast<const char*>(a.stage + (int64_t)row0 * D));
+      if (hm <= 1) {
+        grad_epilogue_cvt<false, false>(acc, hm == 1, rsS, rsS, nullptr, row0, rvalid, D, dw, lw);
+      } else {
+        // scattered rows: offsets from the start of dH (N D 4 < 2^31 with compaction)
+        const auto rsD = make_rsrc(reinterpret_cast<const char*>(
+            COMPACT ? a.dHb : a.dHb + ((int64_t)band.nb0 + row0) * D));
+        grad_epilogue_cvt<false, true>(acc, hm == 2, rsS, rsD,
+                                       COMPACT ? a.rowmap + band.nb0 + row0 : nullptr, row0,
+                                       rvalid, D, dw, lw);
+      }
+    } else {
+      const auto rs = make_rsrc(
+          reinterpret_cast<const char*>(a.dWb + ((int64_t)band.vb0 + row0) * D));
+      grad_epilogue_cvt<true, true>(acc, beta_w != 0, rs, rs, nullptr, row0, rvalid, D, dw, lw);
+    }
+    return;
+  }
   // with compaction the dH^T tile's rows are scattered through the map:
   // offsets from the start of dH (below 2^31 by the planner's check)
   const bool scatter = COMPACT && is_h;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(
       scatter ? dH : out + (int64_t)row0 * D));
-  const int dw = td * kTile + wm * 128 + 4 * (lane >> 5);
-  const int lw = wn * 128 + (lane & 31);
   // Two row groups in flight: the loads of group j + 1 (and j + 2) are out
   // while group j is added and stored.
   auto offsets = [&](int j, uint32_t (&off)[4][4]) {
@@ -886,7 +1014,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
 // [g_grad, G) dZ tiles.
 constexpr int kBandLdsCompact = kDmaLdsBytes + 256 + kGatherTableBytes;   // slots, line touch, map
 
-template <typename T, bool FILTER, bool COMPACT>
+template <typename T, bool FILTER, bool COMPACT, bool BF16G = false>
 __global__ void __launch_bounds__(kThreads, 1)
 bwd_band_kernel(GradArgs<T> ga, DzArgs<T> da, int g_long, int g_grad, int h_first) {
   __shared__ __attribute__((aligned(1024))) char
@@ -899,7 +1027,7 @@ bwd_band_kernel(GradArgs<T> ga, DzArgs<T> da, int g_long, int g_grad, int h_firs
   const int T3 = ga.Td * ga.T3n;   // dH^T tiles
   const bool is_h = h_first ? t < T3 : t >= g_long;
   const int local = h_first ? (is_h ? t : t - T3) : (is_h ? t - g_long : t);
-  grad_tile<T, FILTER, COMPACT>(ga, is_h, local, lds);
+  grad_tile<T, FILTER, COMPACT, BF16G>(ga, is_h, local, lds);
 }
 
 }  // namespace flce

@@ -63,16 +63,21 @@ def test_invalid_shapes(N, D, V, code):
 
 
 def test_invalid_dtype_reduction_flags_eps():
+    import torch
     lib = L.lib()
     info = _abi.FlcePlanInfo()
     d = L.make_desc(8, 64, 10, dtype=7)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_DTYPE
     d = L.make_desc(8, 64, 10, reduction=5)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
-    d = L.make_desc(8, 64, 10, flags=4)
+    d = L.make_desc(8, 64, 10, flags=8)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    # bf16 gradients: bf16 inputs only
+    d = L.make_desc(8, 64, 10, dtype=torch.float32, flags=_abi.FLCE_FLAG_BF16_GRADS)
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    d = L.make_desc(8, 64, 10, flags=_abi.FLCE_FLAG_BF16_GRADS | _abi.FLCE_FLAG_COMPACT_IGNORED)
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_OK
     # row compaction: bf16 only, and 32-bit byte offsets of gathered rows
-    import torch
     d = L.make_desc(8, 64, 10, dtype=torch.float32, flags=_abi.FLCE_FLAG_COMPACT_IGNORED)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
     d = L.make_desc(1 << 18, 2048, 10, flags=_abi.FLCE_FLAG_COMPACT_IGNORED)
@@ -139,6 +144,27 @@ def test_workspace_within_64_mib(name, N, D, V, dt):
     assert p["band_rows"] % 256 == 0 and p["band_vocab"] % 256 == 0
     assert p["n_bands_rows"] * p["band_rows"] >= N and p["n_bands_vocab"] * p["band_vocab"] >= V
     assert p["fwd_band_rows"] % 256 == 0 and p["fwd_band_rows"] >= 256
+
+
+@pytest.mark.parametrize("name,N,D,V", [
+    ("large_vocab", 8192, 2048, 151552), ("long_context", 131072, 2048, 151552),
+    ("wide", 8192, 4096, 128256), ("mid", 4096, 1024, 32000)])
+def test_bf16_gradient_plan_within_64_mib(name, N, D, V):
+    """bf16 gradients: one dZ buffer plus the float dH stage of a token band fit
+    the default budget, and the bands stay wide (the plan is a dZ launch and a
+    gradient launch per band, so a band's tiles should fill the machine)."""
+    p = L.flce_plan(N, D, V, flags=_abi.FLCE_FLAG_BF16_GRADS)
+    assert p["ws_bytes"] <= 64 * MiB
+    stage = p["band_rows"] * D * 4
+    assert p["dz_bytes"] + stage <= p["ws_bytes"]
+    assert p["band_rows"] * p["band_vocab"] >= 4096 * 1024
+    q = L.flce_plan(N, D, V)
+    assert p["ws_bytes"] <= q["ws_bytes"] + 4 * MiB
+
+
+def test_bf16_gradient_plan_at_the_large_vocab_shape():
+    p = L.flce_plan(8192, 2048, 151552, flags=_abi.FLCE_FLAG_BF16_GRADS)
+    assert (p["band_rows"], p["band_vocab"], p["n_bands_rows"]) == (4096, 3840, 2)
 
 
 def test_budget_shrinks_bands_and_reports_overflow():

@@ -1,0 +1,174 @@
+"""bf16 gradient outputs (FLCE_FLAG_BF16_GRADS): dH and dW are written in the
+parameters' type (Cut Cross-Entropy Sec. 5.1 and Table 1 rows 8-10 sum the
+gradients in their final type; the PyTorch 2.13 chapter's section "precision
+policy는 속도 옵션이 아니라 gradient 계약이다" makes the accumulator a stated
+choice).  Here dH of a token band is summed in a float stage and rounded once,
+dW is rounded once per token band.  HIP path vs the fp64 oracle element by
+element, plus the rounding structure against the library's own float path."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import flce_inputs as fi
+import linear_cross_entropy_online_amd as L
+from oracle import flce_oracle as O
+from tests.gpu_util import TOL, max_abs_rel, rel, report
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+B = L.FLCE_FLAG_BF16_GRADS
+C = L.FLCE_FLAG_COMPACT_IGNORED
+
+
+def _dev(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+def _check(name, out, ref, reduction="mean", keep=None):
+    tol = TOL["bf16"]
+    loss, loss_rows, lse, dH, dW = out
+    assert dH.dtype == torch.bfloat16 and dW.dtype == torch.bfloat16
+    k = slice(None) if keep is None else keep
+    vals = dict(lse=max_abs_rel(lse.cpu()[k], ref["lse"][k]),
+                loss_rows=max_abs_rel(loss_rows, ref["loss_rows"]),
+                dH=max_abs_rel(dH, ref["dH"]), dW=max_abs_rel(dW, ref["dW"]))
+    if reduction != "none":
+        vals["loss"] = rel(loss.item(), ref["loss"])
+    report(name, **vals)
+    for key, v in vals.items():
+        assert v <= (tol["grad"] if key in ("dH", "dW") else tol["loss"]), (key, v)
+
+
+def _ulp_bf16(x):
+    """Spacing of bf16 numbers at |x| (8 significant bits); 2^-133 floor."""
+    a = x.abs().double().clamp_min(2.0 ** -126)
+    return torch.exp2(torch.floor(torch.log2(a)) - 7)
+
+
+# budgets that give one, two and many vocabulary bands per token band: the
+# four ways a dH tile ends (stage store / add / add + round / round only)
+@pytest.mark.parametrize("budget,nbv", [(0, "one"), (1 << 20, "many"), (3 << 19, "two")])
+def test_bf16_grads_fused_ragged(budget, nbv):
+    N, D, V = 1500, 264, 3000
+    H, W, y = fi.random_case(N, D, V, seed=51, sigma_w=0.05, ignore_frac=0.05)
+    plan = L.flce_plan(N, D, V, flags=B, ws_budget_bytes=budget)
+    got = plan["n_bands_vocab"]
+    assert (got == 1) if nbv == "one" else (got == 2) if nbv == "two" else (got > 2), plan
+    ref = O.linear_cross_entropy(H, W, y, reduction="mean")
+    Hd, Wd, yd = _dev(H, W, y)
+    out = L.flce_fused_fwd_bwd(Hd, Wd, yd, flags=B, ws_budget_bytes=budget)
+    _check(f"bf16g_fused_{nbv}", out, ref)
+    ign = (y == fi.IGNORE_INDEX).to(DEV)
+    assert torch.all(out[3][ign] == 0)
+
+
+def test_bf16_grads_round_once_structure():
+    """dH is the float sum rounded once: within one bf16 spacing of the float
+    path's dH (the two sum in different band orders, so a value next to a
+    rounding boundary may round the other way).  With one token band dW is
+    rounded once too; with R token bands each rounding moves dW by at most
+    half a spacing of the running sum."""
+    N, D, V = 1100, 264, 9000
+    H, W, y = fi.random_case(N, D, V, seed=52, sigma_w=0.05, ignore_frac=0.05)
+    Hd, Wd, yd = _dev(H, W, y)
+    f = L.flce_fused_fwd_bwd(Hd, Wd, yd)
+    for budget in (0, 1 << 20):
+        plan = L.flce_plan(N, D, V, flags=B, ws_budget_bytes=budget)
+        R = plan["n_bands_rows"]
+        b = L.flce_fused_fwd_bwd(Hd, Wd, yd, flags=B, ws_budget_bytes=budget)
+        # the forward is the same kernel sequence: bitwise equal
+        for i in range(3):
+            assert torch.equal(f[i], b[i])
+        dH32, dW32 = f[3].double(), f[4].double()
+        eH = (b[3].double() - dH32).abs() / _ulp_bf16(f[3])
+        # unit: the spacing at twice the row's largest |dW| (a running sum of
+        # token bands may exceed the final value)
+        eW = (b[4].double() - dW32).abs() / _ulp_bf16(2 * dW32.abs().amax(1, keepdim=True)
+                                                       .expand_as(dW32))
+        report(f"bf16g_rounding_R{R}", dH_ulps=float(eH.max()), dW_ulps_of_rowmax=float(eW.max()))
+        assert float(eH.max()) <= 1.0 + 1e-6
+        assert float(eW.max()) <= R + 1e-6
+
+
+@pytest.mark.parametrize("reduction", ["sum", "none"])
+def test_bf16_grads_separate_backward(reduction):
+    H, W, y = fi.random_case(700, 128, 2100, seed=53, sigma_w=0.08, ignore_frac=0.25)
+    g = torch.Generator().manual_seed(7)
+    dl = torch.randn(700 if reduction == "none" else 1, generator=g, dtype=torch.float64)
+    dlo = dl.numpy() if reduction == "none" else float(dl[0])
+    ref = O.linear_cross_entropy(H, W, y, reduction=reduction, dloss=dlo)
+    Hd, Wd, yd = _dev(H, W, y)
+    loss, loss_rows, lse = L.flce_forward(Hd, Wd, yd, reduction=reduction)
+    dH, dW = L.flce_backward(Hd, Wd, yd, lse, dl.float().to(DEV), reduction=reduction, flags=B,
+                             ws_budget_bytes=1 << 20)
+    _check(f"bf16g_separate_{reduction}", (loss, loss_rows, lse, dH, dW), ref, reduction)
+
+
+def test_bf16_grads_with_compaction():
+    H, W, y = fi.random_case(1500, 264, 3000, seed=54, sigma_w=0.05, ignore_frac=0.6)
+    ref = O.linear_cross_entropy(H, W, y, reduction="mean")
+    Hd, Wd, yd = _dev(H, W, y)
+    keep = (y != fi.IGNORE_INDEX).numpy()
+    for budget in (0, 1 << 20):
+        out = L.flce_fused_fwd_bwd(Hd, Wd, yd, flags=B | C, ws_budget_bytes=budget)
+        _check(f"bf16g_compact_{budget}", out, ref, keep=keep)
+        gone = torch.from_numpy(~keep).to(DEV)
+        assert torch.all(out[3][gone] == 0) and torch.all(out[2][gone] == 0)
+
+
+def test_bf16_grads_with_filter():
+    H, W, y = fi.random_case(640, 128, 20000, seed=55, sigma_w=0.4 / math.sqrt(128),
+                             ignore_frac=0.05)
+    eps = 2.0 ** -12
+    ref = O.linear_cross_entropy(H, W, y, reduction="mean", filter_eps=eps, filter_block=(64, 64))
+    Hd, Wd, yd = _dev(H, W, y)
+    out = L.flce_fused_fwd_bwd(Hd, Wd, yd, filter_eps=eps, flags=B)
+    _check("bf16g_filter", out, ref)
+
+
+def test_bf16_grads_all_rows_ignored_and_empty():
+    H, W, y = fi.random_case(600, 64, 900, seed=56, ignore_frac=1.0)
+    Hd, Wd, yd = _dev(H, W, y)
+    loss, loss_rows, lse, dH, dW = L.flce_fused_fwd_bwd(Hd, Wd, yd, flags=B)
+    assert loss.item() == 0.0 and torch.all(dH == 0) and torch.all(dW == 0)
+    He = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    ye = torch.empty(0, dtype=torch.int64, device=DEV)
+    dW_e = torch.full((900, 64), 3.0, dtype=torch.bfloat16, device=DEV)
+    out = L.flce_fused_fwd_bwd(He, Wd, ye, flags=B,
+                               out=(torch.empty(1, device=DEV), torch.empty(0, device=DEV),
+                                    torch.empty(0, device=DEV),
+                                    torch.empty(0, 64, dtype=torch.bfloat16, device=DEV), dW_e))
+    assert out[0].item() == 0.0 and torch.all(dW_e == 0)
+
+
+def test_scale_gradients_bf16_rounds_once():
+    """bf16 gradients times the upstream scalar: one float multiply, rounded
+    to nearest even (torch's float -> bf16 conversion on the CPU is the same
+    rounding), so the result is exact bit for bit."""
+    g = torch.Generator().manual_seed(8)
+    dH = (torch.randn(300, 264, generator=g) * 3).bfloat16()
+    dW = (torch.randn(1000, 264, generator=g) * 1e-3).bfloat16()
+    s = torch.tensor([-0.7431], dtype=torch.float32)
+    a, b = dH.to(DEV), dW.to(DEV)
+    L.flce_scale_gradients(a, b, s.to(DEV), "mean")
+    assert torch.equal(a.cpu(), (dH.float() * s).bfloat16())
+    assert torch.equal(b.cpu(), (dW.float() * s).bfloat16())
+
+
+@pytest.mark.parametrize("grads_in_forward", [False, True])
+def test_autograd_bf16_grads(grads_in_forward):
+    H, W, y = fi.random_case(900, 136, 5000, seed=57, sigma_w=0.05, ignore_frac=0.05)
+    ref = O.linear_cross_entropy(H, W, y, reduction="mean", dloss=0.5)
+    Hd, Wd, yd = _dev(H, W, y)
+    Hd.requires_grad_(True)
+    Wd.requires_grad_(True)
+    loss = L.linear_cross_entropy(Hd, Wd, yd, grads_in_forward=grads_in_forward, bf16_grads=True)
+    (0.5 * loss).backward()
+    assert Hd.grad.dtype == torch.bfloat16 and Wd.grad.dtype == torch.bfloat16
+    vals = dict(loss=rel(loss.item(), ref["loss"]), dH=max_abs_rel(Hd.grad, ref["dH"]),
+                dW=max_abs_rel(Wd.grad, ref["dW"]))
+    report(f"bf16g_autograd_gif{int(grads_in_forward)}", **vals)
+    assert vals["loss"] <= TOL["bf16"]["loss"]
+    assert vals["dH"] <= TOL["bf16"]["grad"] and vals["dW"] <= TOL["bf16"]["grad"]

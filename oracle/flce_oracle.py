@@ -26,6 +26,10 @@ What it computes, and where the pages define it
   products when every entry satisfies |G| < eps.  eps = 2^-12 is the paper's
   choice.  The block geometry is a parameter (the pages leave it to the
   implementation); blocks are anchored at row 0 and vocabulary index 0.
+  CCE Sec. 5.1 / Table 1 rows 9-10 ("FullC", "FullE") also filter only one
+  of the two products: ``filter_products`` "dH" keeps the exact dW (FullC,
+  C being the classifier W), "dW" keeps the exact dH (FullE, E the
+  embeddings H).
 
 Readings where the pages are silent (each is listed in the design doc):
 * LSE is produced for every row, ignored ones included.
@@ -103,14 +107,16 @@ def _lse(Z: np.ndarray) -> np.ndarray:
 def linear_cross_entropy(H, W, y, ignore_index: int = IGNORE_INDEX_DEFAULT,
                          reduction: str = "mean", dloss=1.0, grads: bool = True,
                          filter_eps: float = 0.0, filter_block=(64, 64),
-                         row_chunk: int = 256):
+                         row_chunk: int = 256, filter_products: str = "both"):
     """Loss, per-row loss, per-row LSE and (optionally) dH, dW in float64.
 
     Returns a dict with keys loss (None for reduction 'none'), loss_rows, lse,
     count, and dH [N,D], dW [V,D] when ``grads``.  With ``filter_eps > 0`` the
     gradient blocks of shape ``filter_block`` (rows x vocab) whose every
-    |softmax - onehot| entry is below ``filter_eps`` are dropped (CCE Alg. 4).
+    |softmax - onehot| entry is below ``filter_eps`` are dropped (CCE Alg. 4)
+    from the products ``filter_products`` names: "both", "dH" or "dW".
     """
+    assert filter_products in ("both", "dH", "dW")
     H = _f64(H)
     W = _f64(W)
     y = _i64(y)
@@ -142,15 +148,20 @@ def linear_cross_entropy(H, W, y, ignore_index: int = IGNORE_INDEX_DEFAULT,
         G = np.exp(Z - lse[r0:r1, None])        # softmax
         G[np.nonzero(vr)[0], y[rows[vr]]] -= 1.0   # - onehot
         G[~vr] = 0.0
+        Gh = Gw = G
         if filter_eps > 0:
+            Gf = G.copy()
             for a in range(0, r1 - r0, nb):
                 for b in range(0, V, vb):
-                    blk = G[a:a + nb, b:b + vb]
+                    blk = Gf[a:a + nb, b:b + vb]
                     if not (np.abs(blk) >= filter_eps).any():
                         blk[...] = 0.0
-        dZ = g[r0:r1, None] * G
-        dH[r0:r1] = dZ @ W
-        dW += dZ.T @ H[r0:r1]
+            if filter_products in ("both", "dH"):
+                Gh = Gf
+            if filter_products in ("both", "dW"):
+                Gw = Gf
+        dH[r0:r1] = (g[r0:r1, None] * Gh) @ W
+        dW += (g[r0:r1, None] * Gw).T @ H[r0:r1]
     if reduction == "mean":
         loss = loss_rows.sum() / max(count, 1)
     elif reduction == "sum":

@@ -207,8 +207,9 @@ def test_reduction_none_matches_sum_with_unit_upstream():
 
 # ------------------------------------------------------------------- filter
 
-def _brute_force_filtered(H, W, y, eps, nb, vb, reduction="mean"):
-    """Element-by-element loops over the definition (small sizes only)."""
+def _brute_force_filtered(H, W, y, eps, nb, vb, reduction="mean", products="both"):
+    """Element-by-element loops over the definition (small sizes only);
+    `products` names the gradient products the dropped blocks leave."""
     N, D = H.shape
     V = W.shape[0]
     valid = [int(t) != -100 for t in y]
@@ -225,6 +226,7 @@ def _brute_force_filtered(H, W, y, eps, nb, vb, reduction="mean"):
         for v in range(V):
             z = sum(H[n, k] * W[v, k] for k in range(D))
             G[n][v] = math.exp(z - lse[n]) - (1.0 if v == y[n] else 0.0)
+    F = [row[:] for row in G]
     for a in range(0, N, nb):
         for b in range(0, V, vb):
             keep = any(abs(G[n][v]) >= eps for n in range(a, min(N, a + nb))
@@ -232,15 +234,17 @@ def _brute_force_filtered(H, W, y, eps, nb, vb, reduction="mean"):
             if not keep:
                 for n in range(a, min(N, a + nb)):
                     for v in range(b, min(V, b + vb)):
-                        G[n][v] = 0.0
+                        F[n][v] = 0.0
+    Gh = F if products in ("both", "dH") else G
+    Gw = F if products in ("both", "dW") else G
     g = (1.0 / max(count, 1)) if reduction == "mean" else 1.0
     dH = np.zeros((N, D))
     dW = np.zeros((V, D))
     for n in range(N):
         for v in range(V):
             for k in range(D):
-                dH[n, k] += g * G[n][v] * W[v, k]
-                dW[v, k] += g * G[n][v] * H[n, k]
+                dH[n, k] += g * Gh[n][v] * W[v, k]
+                dW[v, k] += g * Gw[n][v] * H[n, k]
     return dH, dW
 
 
@@ -256,6 +260,25 @@ def test_filter_brute_force_small_blocks():
     assert not np.allclose(out["dW"], full["dW"], rtol=1e-9, atol=0)   # some blocks dropped
     frac = O.filter_block_stats(H, W, y, full["lse"], eps, block=(4, 4))
     assert 0.0 < frac < 1.0
+
+
+@pytest.mark.parametrize("products,block", [("dH", (4, 2)), ("dW", (2, 4))])
+def test_filter_one_product_brute_force(products, block):
+    """CCE's FullC / FullE: the filter drops blocks from one product only; the
+    other is the exact gradient.  Unequal block shapes catch a transposed
+    block test."""
+    H, W, y = _case(12, 5, 20, seed=16, ignore_frac=0.2, sigma_w=3.0)
+    eps = 0.05
+    out = O.linear_cross_entropy(H, W, y, filter_eps=eps, filter_block=block, row_chunk=4,
+                                 filter_products=products)
+    bdH, bdW = _brute_force_filtered(H, W, y, eps, *block, products=products)
+    assert np.allclose(out["dH"], bdH, rtol=1e-12, atol=1e-15)
+    assert np.allclose(out["dW"], bdW, rtol=1e-12, atol=1e-15)
+    exact_dH, exact_dW = _brute_force_filtered(H, W, y, 0.0, *block)
+    exact, filt = ("dW", "dH") if products == "dH" else ("dH", "dW")
+    ref = {"dH": exact_dH, "dW": exact_dW}
+    assert np.allclose(out[exact], ref[exact], rtol=1e-12, atol=1e-15)
+    assert not np.allclose(out[filt], ref[filt], rtol=1e-9, atol=0)   # blocks were dropped
 
 
 def test_filter_limits():

@@ -81,7 +81,7 @@ enum {
                                       only, and N * D * 4 < 2^31; otherwise
                                       FLCE_E_UNSUPPORTED.  Adds N int32 and
                                       ceil(N/1024) int32 to the workspace.    */
-  FLCE_FLAG_BF16_GRADS = 4u        /* dH and dW are bf16 (the parameters' type)
+  FLCE_FLAG_BF16_GRADS = 4u,       /* dH and dW are bf16 (the parameters' type)
                                       instead of float: the gradient type a
                                       bf16 training loop keeps (CCE Sec. 5.1 with
                                       Table 1 rows 8-10 sums gradients in the
@@ -99,6 +99,20 @@ enum {
                                       The backward then stages one dZ band and
                                       runs each band as a dZ launch followed by
                                       a gradient launch.                     */
+  FLCE_FLAG_FILTER_FULL_C = 8u,    /* with filter_eps > 0: dW (the classifier's
+                                      gradient, CCE's C) is exact and only dH
+                                      is filtered ("FullC", CCE Sec. 5.1 and
+                                      Table 1 row 9).  The dZ band then keeps
+                                      the dropped blocks' values and dH skips
+                                      a 64-wide vocabulary step when the 256
+                                      token rows of its tile are all dropped
+                                      there: dH's filter block is 256 x 64
+                                      (rows x vocabulary, anchored at 0).    */
+  FLCE_FLAG_FILTER_FULL_E = 16u    /* with filter_eps > 0: dH (the embeddings'
+                                      gradient, CCE's E) is exact and only dW
+                                      is filtered ("FullE", Table 1 row 10),
+                                      with a 64 x 256 filter block.  Setting
+                                      both FULL flags is FLCE_E_UNSUPPORTED. */
 };
 
 typedef struct flce_desc {

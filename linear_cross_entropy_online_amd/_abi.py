@@ -14,6 +14,8 @@ FLCE_MEAN, FLCE_SUM, FLCE_NONE = 0, 1, 2
 FLCE_FLAG_PROFILE = 1
 FLCE_FLAG_COMPACT_IGNORED = 2
 FLCE_FLAG_BF16_GRADS = 4
+FLCE_FLAG_FILTER_FULL_C = 8
+FLCE_FLAG_FILTER_FULL_E = 16
 (FLCE_K_FWD_LSE, FLCE_K_LSE_COMBINE, FLCE_K_FINALIZE, FLCE_K_BWD_DZ, FLCE_K_BWD_GRAD,
  FLCE_K_AUX, FLCE_K_BWD_BAND, FLCE_K_COUNT) = range(8)
 

@@ -65,8 +65,11 @@ int validate(const flce_desc* d) {
   if (d->hidden < 8 || d->hidden % 8 != 0 || d->hidden >= (int64_t(1) << 20)) return FLCE_E_SHAPE;
   if (d->in_dtype != FLCE_BF16 && d->in_dtype != FLCE_F32) return FLCE_E_DTYPE;
   if (d->reduction < FLCE_MEAN || d->reduction > FLCE_NONE) return FLCE_E_UNSUPPORTED;
-  if (d->flags & ~uint32_t(FLCE_FLAG_PROFILE | FLCE_FLAG_COMPACT_IGNORED | FLCE_FLAG_BF16_GRADS))
+  constexpr uint32_t full = FLCE_FLAG_FILTER_FULL_C | FLCE_FLAG_FILTER_FULL_E;
+  if (d->flags & ~uint32_t(FLCE_FLAG_PROFILE | FLCE_FLAG_COMPACT_IGNORED | FLCE_FLAG_BF16_GRADS |
+                           full))
     return FLCE_E_UNSUPPORTED;
+  if ((d->flags & full) == full) return FLCE_E_UNSUPPORTED;
   if ((d->flags & FLCE_FLAG_BF16_GRADS) && d->in_dtype != FLCE_BF16) return FLCE_E_UNSUPPORTED;
   if (d->flags & FLCE_FLAG_COMPACT_IGNORED) {
     // bf16 core only; gathered H rows and scattered dH rows use 32-bit byte offsets
@@ -360,6 +363,10 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
   const int Td = int(cdiv(D, flce::kTile));
   const int nb = p.nbn * p.nbv;
   const bool filt = d->filter_eps > 0.f;
+  // filter on one product only (CCE FullC / FullE): dZ keeps every value
+  const int skip_h = (d->flags & FLCE_FLAG_FILTER_FULL_E) ? 0 : 1;
+  const int skip_w = (d->flags & FLCE_FLAG_FILTER_FULL_C) ? 0 : 1;
+  const int keep_dropped = skip_h && skip_w ? 0 : 1;
   if (w.rowmap)   // dH rows of ignored rows: no tile writes them
     FLCE_TRY(launch(FLCE_K_AUX, prof, s, [&] {
       flce::zero_ignored_rows_kernel<<<dim3(int(cdiv(N, 16))), dim3(256), 0, s>>>(
@@ -372,7 +379,7 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
     return flce::DzArgs<T>{static_cast<const T*>(H), static_cast<const T*>(W), y, lse, dloss_rows,
                            w.hdr, N, D, V, d->ignore_index, d->reduction, d->filter_eps, band,
                            TMv, TNn, reinterpret_cast<T*>(w.dz[buf]), w.flags[buf],
-                           w.flagsT[buf], w.rowmap};
+                           w.flagsT[buf], w.rowmap, keep_dropped};
   };
   // gradient tiles of band k reading buffer `buf`; g_long, g_grad, h_first out
   auto grad_args = [&](int k, int buf, int& g_long, int& g_grad, int& h_first) {
@@ -389,7 +396,7 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
                              reinterpret_cast<const T*>(w.dz[buf]), w.flags[buf], w.flagsT[buf],
                              p.bf16g ? nullptr : static_cast<float*>(dH),
                              p.bf16g ? nullptr : static_cast<float*>(dW), N, D, V, band, T3n, T2n,
-                             Td, bv > 0 ? 1 : 0, bn > 0 ? 1 : 0, w.rowmap, w.hdr,
+                             Td, bv > 0 ? 1 : 0, bn > 0 ? 1 : 0, skip_h, skip_w, w.rowmap, w.hdr,
                              p.bf16g ? static_cast<uint16_t*>(dH) : nullptr,
                              p.bf16g ? static_cast<uint16_t*>(dW) : nullptr, w.stage, h_mode};
   };

@@ -526,6 +526,7 @@ struct DzArgs {
   uint8_t* flags;        // [frows][fcols]
   uint8_t* flagsT;       // [fcols][frows]
   const int* rowmap;     // row compaction: band rows are positions of rowmap (else rows)
+  int keep_dropped;      // store dropped blocks' dZ too (filter on one product only)
 };
 
 // dZ tile t of a band: Z = W_v H_n^T recomputed, G = softmax(Z) - onehot(y),
@@ -629,13 +630,15 @@ __device__ __forceinline__ void dz_tile(const DzArgs<T>& a, int t, char* lds) {
     }
     // CCE Alg. 4 filter on 64x64 blocks: dropped iff every |G| < eps (an
     // all-zero block is dropped too, which changes nothing).  Dropped blocks
-    // are written as zeros and flagged so the contractions can skip them.
+    // are written as zeros and flagged so the contractions can skip them;
+    // with keep_dropped (filter on one product only) their values are kept
+    // and only the filtered product skips.
     float gk[2][2];
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
       const bool kp = __any((kmax[bi] > 0.f && kmax[bi] >= eps) || bad[2 * bj] || bad[2 * bj + 1]);
-      gk[bi][0] = kp ? g[2 * bj] : 0.f;
-      gk[bi][1] = kp ? g[2 * bj + 1] : 0.f;
+      gk[bi][0] = kp || a.keep_dropped ? g[2 * bj] : 0.f;
+      gk[bi][1] = kp || a.keep_dropped ? g[2 * bj + 1] : 0.f;
       if (lane == 0) {
         const int fr = fr0 + bj, fc = fc0 + bi;
         flags[fr * band.fcols + fc] = kp ? 0 : 1;
@@ -698,6 +701,7 @@ struct SkipRowsOfFlags {
   static constexpr int kMaxBlocks = 128;              // K <= 8192
   const uint8_t* base;     // first of the four flags of 64-block 0
   int step_stride;         // bytes between consecutive 64-blocks
+  int all = 0;             // every step active (the product is not filtered)
   uint64_t lo = 0, hi = 0; // bit b of (hi:lo): 64-block b is active
   __device__ __forceinline__ void prepare(int nsteps) {
     const int nb = (nsteps + (1 << kShift) - 1) >> kShift;
@@ -710,8 +714,11 @@ struct SkipRowsOfFlags {
       const uint32_t f = *reinterpret_cast<const uint32_t*>(base + b * step_stride);
       m1 |= (uint64_t)(f != 0x01010101u) << (b - 64);
     }
-    lo = m0;
-    hi = m1;
+    // (a select, not a branch: a branch here makes the compiler treat the
+    // tile's operand descriptors as divergent)
+    const uint64_t every = all ? ~0ull : 0ull;
+    lo = m0 | every;
+    hi = m1 | every;
   }
   __device__ __forceinline__ bool operator()(int s) const {
     const int b = s >> kShift;
@@ -755,6 +762,7 @@ struct GradArgs {
   BandArgs band;
   int T3n, T2n, Td;        // token-row tiles, vocabulary tiles, d tiles of the band
   int beta_h, beta_w;      // accumulate into dH / dW (else overwrite)
+  int skip_h, skip_w;      // FILTER: the product skips dropped K steps (else exact)
   const int* rowmap;       // row compaction (COMPACT): band rows are positions of rowmap
   const Header* hdr;       // nvalid with row compaction
   // bf16 gradients (BF16G): dH, dW are bf16; dH of the token band is summed in
@@ -882,7 +890,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
     const int kpad = (band.vs_cur + kTile - 1) / kTile * kTile;
     const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T3n * kTile, kpad};
     if constexpr (FILTER) {
-      const SkipRowsOfFlags<step_k<T>()> act{flagsT + tr * 4, band.frows};
+      const SkipRowsOfFlags<step_k<T>()> act{flagsT + tr * 4, band.frows, !a.skip_h};
       tile_contract<T, true, false>(A, B, td * kTile, tr * kTile, band.vs_cur, act, acc, lds);
     } else {
       tile_contract<T, true, false>(A, B, td * kTile, tr * kTile, band.vs_cur, AllActive{}, acc,
@@ -902,7 +910,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
                       reinterpret_cast<const int*>(table), half};
       const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2n * kTile, K};
       if constexpr (FILTER) {
-        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols};
+        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols, !a.skip_w};
         tile_contract<T, true, true, SkipRowsOfFlags<step_k<T>()>, true>(A, B, td * kTile,
                                                                         tr * kTile, K, act, acc,
                                                                         lds);
@@ -914,7 +922,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
       const Operand A{reinterpret_cast<const char*>(H + (int64_t)band.nb0 * D), D, D, band.ns_cur};
       const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2n * kTile, band.ns_cur};
       if constexpr (FILTER) {
-        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols};
+        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols, !a.skip_w};
         tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, act, acc, lds);
       } else {
         tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, AllActive{}, acc,

@@ -70,8 +70,14 @@ def test_invalid_dtype_reduction_flags_eps():
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_DTYPE
     d = L.make_desc(8, 64, 10, reduction=5)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
-    d = L.make_desc(8, 64, 10, flags=8)
+    d = L.make_desc(8, 64, 10, flags=32)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    # a filter on one product: C or E, not both
+    d = L.make_desc(8, 64, 10, flags=_abi.FLCE_FLAG_FILTER_FULL_C | _abi.FLCE_FLAG_FILTER_FULL_E)
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    for f in (_abi.FLCE_FLAG_FILTER_FULL_C, _abi.FLCE_FLAG_FILTER_FULL_E):
+        d = L.make_desc(8, 64, 10, filter_eps=2.0 ** -12, flags=f)
+        assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_OK
     # bf16 gradients: bf16 inputs only
     d = L.make_desc(8, 64, 10, dtype=torch.float32, flags=_abi.FLCE_FLAG_BF16_GRADS)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED

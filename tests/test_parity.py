@@ -192,6 +192,39 @@ def test_filter_matches_filtered_oracle():
     _check_against_oracle("filter_vs_filtered_oracle", H, W, y, out, ref, "bf16")
 
 
+@pytest.mark.parametrize("mode", ["full_c", "full_e", "full_c_bf16_grads"])
+def test_filter_on_one_product(mode):
+    """CCE's FullC / FullE: one product is exact (bit for bit the unfiltered
+    call's), the other is filtered; with the dZ band unzeroed, that product
+    drops a 64-wide K step when its tile's 256 rows (dH) or 256 vocabulary
+    rows (dW) are all dropped there, i.e. filter blocks of 256 x 64 (dH) and
+    64 x 256 (dW), against the oracle's one-product filter."""
+    H, W, y = fi.random_case(640, 128, 20000, seed=28, sigma_w=0.4 / math.sqrt(128))
+    Hd, Wd, yd = _dev(H, W, y)
+    eps = 2.0 ** -12
+    full_c = mode.startswith("full_c")
+    flags = L.FLCE_FLAG_FILTER_FULL_C if full_c else L.FLCE_FLAG_FILTER_FULL_E
+    products, block = ("dH", (256, 64)) if full_c else ("dW", (64, 256))
+    if mode.endswith("bf16_grads"):
+        flags |= L.FLCE_FLAG_BF16_GRADS
+    base = L.flce_fused_fwd_bwd(Hd, Wd, yd, flags=flags & L.FLCE_FLAG_BF16_GRADS)
+    out = L.flce_fused_fwd_bwd(Hd, Wd, yd, filter_eps=eps, flags=flags)
+    ref = O.linear_cross_entropy(H, W, y, filter_eps=eps, filter_block=block,
+                                 filter_products=products)
+    full = O.linear_cross_entropy(H, W, y)
+    frac = O.filter_block_stats(H, W, y, full["lse"], eps, block=block)
+    exact = 4 if full_c else 3
+    report(mode, skip_frac=frac, filtered_vs_exact=max_abs_rel(out[7 - exact], full[products]))
+    assert frac > 0.05
+    assert torch.equal(out[exact], base[exact])
+    if flags & L.FLCE_FLAG_BF16_GRADS:
+        tol = TOL["bf16"]["grad"]
+        for i, k in ((3, "dH"), (4, "dW")):
+            assert max_abs_rel(out[i], ref[k]) <= tol, k
+    else:
+        _check_against_oracle(mode, H, W, y, out, ref, "bf16")
+
+
 def test_invalid_target_sets_status():
     H, W, y = fi.random_case(300, 64, 500, seed=29, ignore_frac=0.0)
     y[17] = 500

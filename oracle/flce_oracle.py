@@ -30,6 +30,10 @@ What it computes, and where the pages define it
   of the two products: ``filter_products`` "dH" keeps the exact dW (FullC,
   C being the classifier W), "dW" keeps the exact dH (FullE, E the
   embeddings H).
+* Vocabulary sorting.  CCE Sec. 4.3 ("Vocabulary sorting"): the vocabulary
+  is ordered by each entry's average logit over the batch, and the filter's
+  vocabulary blocks are taken over that order instead of the natural one,
+  so that entries with non-trivial gradients share blocks.
 
 Readings where the pages are silent (each is listed in the design doc):
 * LSE is produced for every row, ignored ones included.
@@ -37,6 +41,10 @@ Readings where the pages are silent (each is listed in the design doc):
   with no non-ignored row is dropped (its dZ is zero either way).
 * Upstream gradient ``dloss``: a scalar for mean/sum, one value per row for
   reduction "none"; defaults to 1.
+* Vocabulary sorting: the average is over the non-ignored rows (the rows
+  whose gradients the filter acts on); the order is by decreasing average,
+  ties by increasing vocabulary index; blocks of consecutive sorted
+  positions start at position 0.
 
 Method: inputs are upcast exactly to float64; logits are materialised one row
 chunk at a time (``Z = H_chunk @ W^T`` via numpy's matmul); max-shifted
@@ -107,14 +115,17 @@ def _lse(Z: np.ndarray) -> np.ndarray:
 def linear_cross_entropy(H, W, y, ignore_index: int = IGNORE_INDEX_DEFAULT,
                          reduction: str = "mean", dloss=1.0, grads: bool = True,
                          filter_eps: float = 0.0, filter_block=(64, 64),
-                         row_chunk: int = 256, filter_products: str = "both"):
+                         row_chunk: int = 256, filter_products: str = "both",
+                         sort_vocab: bool = False):
     """Loss, per-row loss, per-row LSE and (optionally) dH, dW in float64.
 
     Returns a dict with keys loss (None for reduction 'none'), loss_rows, lse,
     count, and dH [N,D], dW [V,D] when ``grads``.  With ``filter_eps > 0`` the
     gradient blocks of shape ``filter_block`` (rows x vocab) whose every
     |softmax - onehot| entry is below ``filter_eps`` are dropped (CCE Alg. 4)
-    from the products ``filter_products`` names: "both", "dH" or "dW".
+    from the products ``filter_products`` names: "both", "dH" or "dW".  With
+    ``sort_vocab`` the vocabulary blocks are consecutive positions of
+    ``vocab_order`` (CCE Sec. 4.3) instead of consecutive indices.
     """
     assert filter_products in ("both", "dH", "dW")
     H = _f64(H)
@@ -129,6 +140,8 @@ def linear_cross_entropy(H, W, y, ignore_index: int = IGNORE_INDEX_DEFAULT,
     nb, vb = filter_block
     if filter_eps > 0:
         row_chunk = max(nb, (row_chunk // nb) * nb)   # chunk edges on block edges
+    order = vocab_order(H, W, y, ignore_index, row_chunk) if sort_vocab and filter_eps > 0 \
+        else np.arange(V)
 
     lse = np.empty(N)
     loss_rows = np.zeros(N)
@@ -150,12 +163,13 @@ def linear_cross_entropy(H, W, y, ignore_index: int = IGNORE_INDEX_DEFAULT,
         G[~vr] = 0.0
         Gh = Gw = G
         if filter_eps > 0:
-            Gf = G.copy()
+            Gf = G[:, order]                    # columns in block order
             for a in range(0, r1 - r0, nb):
                 for b in range(0, V, vb):
                     blk = Gf[a:a + nb, b:b + vb]
                     if not (np.abs(blk) >= filter_eps).any():
                         blk[...] = 0.0
+            Gf = Gf[:, np.argsort(order)]       # back to vocabulary indices
             if filter_products in ("both", "dH"):
                 Gh = Gf
             if filter_products in ("both", "dW"):
@@ -173,6 +187,24 @@ def linear_cross_entropy(H, W, y, ignore_index: int = IGNORE_INDEX_DEFAULT,
         out["dH"] = dH
         out["dW"] = dW
     return out
+
+
+def vocab_order(H, W, y, ignore_index: int = IGNORE_INDEX_DEFAULT, row_chunk: int = 256):
+    """Vocabulary indices by decreasing average logit over the non-ignored
+    rows, ties by increasing index (CCE Sec. 4.3, vocabulary sorting)."""
+    H = _f64(H)
+    W = _f64(W)
+    y = _i64(y)
+    V = W.shape[0]
+    valid = valid_rows(y, V, ignore_index)
+    count = int(valid.sum())
+    total = np.zeros(V)
+    for r0 in range(0, H.shape[0], row_chunk):
+        r1 = min(H.shape[0], r0 + row_chunk)
+        Z = H[r0:r1] @ W.T
+        total += Z[valid[r0:r1]].sum(axis=0)
+    avg = total / max(count, 1)
+    return np.argsort(-avg, kind="stable")
 
 
 # ---------------------------------------------------------------------------

@@ -281,6 +281,90 @@ def test_filter_one_product_brute_force(products, block):
     assert not np.allclose(out[filt], ref[filt], rtol=1e-9, atol=0)   # blocks were dropped
 
 
+def _brute_force_sorted_filtered(H, W, y, eps, nb, vb):
+    """Vocabulary sorting by loops: average logit of each vocabulary entry over
+    the non-ignored rows, positions by (decreasing average, index), the filter
+    on blocks of consecutive positions; mean reduction."""
+    N, D = H.shape
+    V = W.shape[0]
+    valid = [int(t) != -100 for t in y]
+    count = sum(valid)
+    z = [[sum(H[n, k] * W[v, k] for k in range(D)) for v in range(V)] for n in range(N)]
+    avg = [sum(z[n][v] for n in range(N) if valid[n]) / max(count, 1) for v in range(V)]
+    order = sorted(range(V), key=lambda v: (-avg[v], v))
+    G = [[0.0] * V for _ in range(N)]
+    for n in range(N):
+        m = max(z[n])
+        lse = m + math.log(sum(math.exp(t - m) for t in z[n]))
+        if valid[n]:
+            for v in range(V):
+                G[n][v] = math.exp(z[n][v] - lse) - (1.0 if v == y[n] else 0.0)
+    for a in range(0, N, nb):
+        for b in range(0, V, vb):
+            cols = order[b:b + vb]
+            rows = range(a, min(N, a + nb))
+            if not any(abs(G[n][v]) >= eps for n in rows for v in cols):
+                for n in rows:
+                    for v in cols:
+                        G[n][v] = 0.0
+    g = 1.0 / max(count, 1)
+    dH = np.zeros((N, D))
+    dW = np.zeros((V, D))
+    for n in range(N):
+        for v in range(V):
+            for k in range(D):
+                dH[n, k] += g * G[n][v] * W[v, k]
+                dW[v, k] += g * G[n][v] * H[n, k]
+    return order, dH, dW
+
+
+def test_sorted_vocabulary_filter_brute_force():
+    H, W, y = _case(12, 5, 20, seed=17, ignore_frac=0.2, sigma_w=3.0)
+    eps = 0.05
+    order, bdH, bdW = _brute_force_sorted_filtered(H, W, y, eps, 4, 4)
+    assert list(O.vocab_order(H, W, y, row_chunk=4)) == order
+    assert order != sorted(order)          # the sort moved something
+    out = O.linear_cross_entropy(H, W, y, filter_eps=eps, filter_block=(4, 4), row_chunk=4,
+                                 sort_vocab=True)
+    assert np.allclose(out["dH"], bdH, rtol=1e-12, atol=1e-15)
+    assert np.allclose(out["dW"], bdW, rtol=1e-12, atol=1e-15)
+    plain = O.linear_cross_entropy(H, W, y, filter_eps=eps, filter_block=(4, 4), row_chunk=4)
+    assert not np.allclose(out["dW"], plain["dW"], rtol=1e-9, atol=0)
+    # without the filter the order changes nothing
+    a = O.linear_cross_entropy(H, W, y, sort_vocab=True)
+    b = O.linear_cross_entropy(H, W, y)
+    assert np.array_equal(a["dH"], b["dH"]) and np.array_equal(a["dW"], b["dW"])
+
+
+def test_sorted_vocabulary_groups_the_likely_tokens():
+    """Entries with a high average logit end up in the leading blocks: when a
+    few scattered vocabulary entries carry the whole softmax for every row,
+    sorting packs them into one block, so the filter drops every other block
+    (CCE's purpose for the sort)."""
+    rng = np.random.default_rng(3)
+    N, D, V = 16, 4, 64
+    H = np.ones((N, D)) + 0.01 * rng.standard_normal((N, D))
+    W = np.zeros((V, D))
+    hot = [5, 21, 38, 60]                 # one per natural block of 16
+    W[hot] = 4.0
+    y = np.array([hot[i % 4] for i in range(N)])
+    order = O.vocab_order(H, W, y)
+    assert sorted(order[:4].tolist()) == hot
+    full = O.linear_cross_entropy(H, W, y)
+    eps = 1e-6
+    srt = O.linear_cross_entropy(H, W, y, filter_eps=eps, filter_block=(16, 16), sort_vocab=True)
+    nat = O.linear_cross_entropy(H, W, y, filter_eps=eps, filter_block=(16, 16))
+    cold = order[16:]
+    assert np.all(np.abs(full["dW"][cold]) > 0)
+    # natural blocks each hold a hot entry: nothing dropped (the same sums up
+    # to the matmul's rounding order)
+    assert np.allclose(nat["dW"], full["dW"], rtol=1e-9, atol=0)
+    # sorted: the block of hot entries is kept, the three cold blocks
+    # (|G| ~ 3e-8 < eps) are dropped
+    assert np.all(srt["dW"][cold] == 0)
+    assert np.allclose(srt["dW"][hot], full["dW"][hot], rtol=1e-9, atol=0)
+
+
 def test_filter_limits():
     H, W, y = _case(16, 6, 24, seed=14)
     full = O.linear_cross_entropy(H, W, y, row_chunk=8)

@@ -139,6 +139,24 @@ def random_case(n: int, d: int, v: int, seed: int, dtype: str = "bf16", sigma_w:
     return H.to(dt), W.to(dt), y
 
 
+def dyadic_case(n: int, d: int, v: int, seed: int, ignore_frac: float = 0.05):
+    """Inputs on a dyadic grid: H = (a + k) / 8 with a fixed per-column offset a
+    and k uniform in [-4, 4], W = j / 32 with j uniform in [-4, 4].  Every
+    product is a multiple of 2^-8 and every sum of them over rows or columns
+    at these sizes stays below 2^16, so it is exact in float32 whatever the
+    order (the offset gives the vocabulary entries distinct average logits,
+    with ties)."""
+    g = torch.Generator().manual_seed(seed)
+    a = torch.randint(-2, 3, (1, d), generator=g).float()
+    H = (a + torch.randint(-4, 5, (n, d), generator=g).float()) / 8
+    W = torch.randint(-4, 5, (v, d), generator=g).float() / 32
+    y = torch.randint(0, v, (n,), generator=g, dtype=torch.int64)
+    n_ign = int(round(ignore_frac * n))
+    if n_ign:
+        y[torch.randperm(n, generator=g)[:n_ign]] = IGNORE_INDEX
+    return H.to(torch.bfloat16), W.to(torch.bfloat16), y
+
+
 def full_logits_bytes(n: int, v: int, elem_bytes: int = 2) -> int:
     """Size of an [N, V] logits tensor, the buffer the fused path never builds."""
     return n * v * elem_bytes

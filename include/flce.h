@@ -108,11 +108,29 @@ enum {
                                       token rows of its tile are all dropped
                                       there: dH's filter block is 256 x 64
                                       (rows x vocabulary, anchored at 0).    */
-  FLCE_FLAG_FILTER_FULL_E = 16u    /* with filter_eps > 0: dH (the embeddings'
+  FLCE_FLAG_FILTER_FULL_E = 16u,   /* with filter_eps > 0: dH (the embeddings'
                                       gradient, CCE's E) is exact and only dW
                                       is filtered ("FullE", Table 1 row 10),
                                       with a 64 x 256 filter block.  Setting
                                       both FULL flags is FLCE_E_UNSUPPORTED. */
+  FLCE_FLAG_SORT_VOCAB = 32u       /* with filter_eps > 0: the filter's
+                                      vocabulary blocks are taken over the
+                                      vocabulary ordered by decreasing average
+                                      logit over the non-ignored rows (ties by
+                                      increasing index) instead of the natural
+                                      order (CCE Sec. 4.3, "Vocabulary
+                                      sorting").  The backward first computes
+                                      the order (sum of the kept rows of H,
+                                      one product with W, a stable radix
+                                      sort); its bands then hold sorted
+                                      positions.  bf16 inputs and V * D * 4 <
+                                      2^31 only, else FLCE_E_UNSUPPORTED; the
+                                      bands' vocabulary width is capped at
+                                      4096.  Adds 2 V int32 to the workspace
+                                      (the order, at
+                                      flce_plan_info.vocab_order_offset, and
+                                      its inverse).  No effect without the
+                                      filter.                                */
 };
 
 typedef struct flce_desc {
@@ -144,6 +162,10 @@ typedef struct flce_plan_info {
   int32_t filter_block;    /* edge of a filter block (64)                      */
   int64_t dz_bytes;        /* bytes of one staged dZ band buffer (two of them,
                               or one with FLCE_FLAG_BF16_GRADS)                */
+  int64_t vocab_order_offset; /* FLCE_FLAG_SORT_VOCAB with the filter: byte
+                              offset in ws of the int32 [V] sorted vocabulary
+                              (position -> vocabulary row) a backward leaves
+                              there; else -1                                 */
 } flce_plan_info;
 
 /* Exact workspace size for *d (the maximum over the three compute entry

@@ -14,6 +14,8 @@
 //                        ceil(NS/256), writing buffer k % 2); nb + 1 launches
 //     (bf16 gradients: one dZ buffer, and per band a dZ launch then a
 //     gradient launch; dH of the token band summed in a float stage)
+//   (sorted vocabulary, before the bands: colsum_partial/final_kernel,
+//    vocab_key_kernel, 4 x sort_hist/scan/scatter_kernel, invert_perm_kernel)
 // dH of a token band accumulates over the vocabulary bands and dW of a
 // vocabulary band over the token bands; the first contribution stores, the
 // rest add, all in stream order, so the result is deterministic.
@@ -27,6 +29,7 @@
 
 #include "../../include/flce.h"
 #include "kernels.hpp"
+#include "vocab_sort.hpp"
 
 namespace {
 
@@ -34,6 +37,7 @@ constexpr uint64_t kDefaultBudget = 64ull << 20;
 constexpr int kFilterBlock = 64;
 constexpr int kMaxBandRows = 4096;    // NS: token rows of a backward band
 constexpr int kMaxBandVocab = 8192;   // VS: the filter's K-skip masks cover K <= 8192
+constexpr int kMaxBandVocabSorted = 4096;   // VS with a sorted vocabulary: LDS row table
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -52,6 +56,9 @@ struct Plan {
   size_t flag_bytes;   // one flag grid
   bool compact;        // ignored rows compacted away (row map in the workspace)
   bool bf16g;          // bf16 gradients: one dZ buffer + a float dH stage
+  bool sort;           // sorted vocabulary (with the filter)
+  int nsblk;           // radix-sort blocks
+  size_t off_vperm, off_vinv, sort_bytes;
   int ncblk;           // compaction blocks
   size_t stage_bytes;  // the dH stage of one token band (bf16 gradients)
   size_t off_rowmap, off_cblk;
@@ -67,10 +74,15 @@ int validate(const flce_desc* d) {
   if (d->reduction < FLCE_MEAN || d->reduction > FLCE_NONE) return FLCE_E_UNSUPPORTED;
   constexpr uint32_t full = FLCE_FLAG_FILTER_FULL_C | FLCE_FLAG_FILTER_FULL_E;
   if (d->flags & ~uint32_t(FLCE_FLAG_PROFILE | FLCE_FLAG_COMPACT_IGNORED | FLCE_FLAG_BF16_GRADS |
-                           full))
+                           FLCE_FLAG_SORT_VOCAB | full))
     return FLCE_E_UNSUPPORTED;
   if ((d->flags & full) == full) return FLCE_E_UNSUPPORTED;
   if ((d->flags & FLCE_FLAG_BF16_GRADS) && d->in_dtype != FLCE_BF16) return FLCE_E_UNSUPPORTED;
+  if (d->flags & FLCE_FLAG_SORT_VOCAB) {
+    // bf16 core only; gathered W rows and scattered dW rows use 32-bit byte offsets
+    if (d->in_dtype != FLCE_BF16) return FLCE_E_UNSUPPORTED;
+    if (d->vocab * d->hidden * 4 >= (int64_t(1) << 31)) return FLCE_E_UNSUPPORTED;
+  }
   if (d->flags & FLCE_FLAG_COMPACT_IGNORED) {
     // bf16 core only; gathered H rows and scattered dH rows use 32-bit byte offsets
     if (d->in_dtype != FLCE_BF16) return FLCE_E_UNSUPPORTED;
@@ -89,6 +101,15 @@ int validate(const flce_desc* d) {
 // stage of a token band (NS x D).
 size_t backward_bytes(const Plan& p) {
   return p.bf16g ? p.dz_bytes + p.stage_bytes : 2 * p.dz_bytes;
+}
+
+// Scratch of the vocabulary sort, at the start of `big` (used before the first
+// dZ band): keys x 2, indices, histograms, column-sum partials, column sums.
+size_t sort_scratch(const Plan& p) {
+  if (!p.sort) return 0;
+  const size_t V = size_t(p.V);
+  return align256(V * 4) * 3 + align256(size_t(256) * p.nsblk * 4) +
+         align256(size_t(flce::kColSplits) * p.D * 4) + align256(size_t(p.D) * 4);
 }
 
 // Forward band rows: as many as the backward part of `big` holds partials
@@ -121,10 +142,18 @@ size_t layout(Plan& p) {
     p.off_cblk = o;
     o = align256(o + size_t(p.ncblk) * 4);
   }
+  p.off_vperm = p.off_vinv = o;
+  if (p.sort) {
+    p.off_vperm = o;
+    o = align256(o + size_t(p.V) * 4);
+    p.off_vinv = o;
+    o = align256(o + size_t(p.V) * 4);
+  }
   p.off_big = o;
   p.dz_bytes = align256(size_t(p.NS) * p.VS * p.es);
   p.stage_bytes = p.bf16g ? align256(size_t(p.NS) * p.D * 4) : 0;
-  p.big = std::max(backward_bytes(p), size_t(2) * p.Tv * p.NF * 4);
+  p.sort_bytes = sort_scratch(p);
+  p.big = std::max({backward_bytes(p), size_t(2) * p.Tv * p.NF * 4, p.sort_bytes});
   o = align256(o + p.big);
   p.total = o;
   return o;
@@ -149,6 +178,8 @@ int make_plan(const flce_desc* d, Plan& p) {
   p.es = d->in_dtype == FLCE_BF16 ? 2 : 4;
   p.compact = (d->flags & FLCE_FLAG_COMPACT_IGNORED) != 0;
   p.bf16g = (d->flags & FLCE_FLAG_BF16_GRADS) != 0;
+  p.sort = (d->flags & FLCE_FLAG_SORT_VOCAB) != 0 && d->filter_eps > 0.f;
+  p.nsblk = int(cdiv(p.V, flce::kSortTile));
   p.ncblk = int(cdiv(std::max<int64_t>(p.N, 1), flce::kCompactRows));
   p.Tv = int(cdiv(p.V, flce::kTile));
   const int64_t Npad = cdiv(std::max<int64_t>(p.N, 1), 256) * 256;
@@ -159,7 +190,8 @@ int make_plan(const flce_desc* d, Plan& p) {
   // rows) down by halves, VS is the widest multiple of 256 that fits; the
   // first NS whose VS is at least NS / 2 is taken.
   const uint64_t budget = d->ws_budget_bytes ? d->ws_budget_bytes : kDefaultBudget;
-  const int vs_cap = int(std::min<int64_t>(kMaxBandVocab, cdiv(p.V, 256) * 256));
+  const int vs_cap = int(std::min<int64_t>(p.sort ? kMaxBandVocabSorted : kMaxBandVocab,
+                                           cdiv(p.V, 256) * 256));
   auto fits = [&](int ns, int vs) {
     p.NS = ns;
     p.VS = vs;
@@ -239,6 +271,10 @@ struct Ws {
   uint8_t *flags[2], *flagsT[2];
   char* dz[2];    // the same buffer twice with bf16 gradients
   float* stage;  // dH stage of a token band (bf16 gradients)
+  int *vperm, *vinv;   // sorted vocabulary (null otherwise)
+  uint32_t *keys[2], *hist;
+  int* idx;            // sort ping-pong indices (the other half is vperm)
+  float *part, *hbar;
   int* rowmap;   // null without compaction
   int* cblk;
 };
@@ -259,6 +295,18 @@ Ws carve(const Plan& p, void* ws) {
     w.dz[k] = b + p.off_big + (p.bf16g ? 0 : k * p.dz_bytes);
   }
   w.stage = p.bf16g ? reinterpret_cast<float*>(b + p.off_big + p.dz_bytes) : nullptr;
+  w.vperm = p.sort ? reinterpret_cast<int*>(b + p.off_vperm) : nullptr;
+  w.vinv = p.sort ? reinterpret_cast<int*>(b + p.off_vinv) : nullptr;
+  {
+    char* q = b + p.off_big;
+    const size_t kv = align256(size_t(p.V) * 4);
+    w.keys[0] = reinterpret_cast<uint32_t*>(q);
+    w.keys[1] = reinterpret_cast<uint32_t*>(q + kv);
+    w.idx = reinterpret_cast<int*>(q + 2 * kv);
+    w.hist = reinterpret_cast<uint32_t*>(q + 3 * kv);
+    w.part = reinterpret_cast<float*>(q + 3 * kv + align256(size_t(256) * p.nsblk * 4));
+    w.hbar = w.part + size_t(flce::kColSplits) * p.D;
+  }
   return w;
 }
 
@@ -320,13 +368,64 @@ flce::BandArgs band_args(const Plan& p, int k) {
   return band;
 }
 
+// The sorted vocabulary (CCE Sec. 4.3): key_v = W_v . sum of the kept rows
+// of H, then a stable LSD radix sort by decreasing key (4 passes of 8 bits;
+// indices ping-pong between the scratch and vperm, ending in vperm), then
+// its inverse.
+int run_sort(const flce_desc* d, const Plan& p, const void* H, const void* W, const int64_t* y,
+             const Ws& w, bool prof, hipStream_t s) {
+  const int N = int(p.N), D = int(p.D), V = int(p.V);
+  const auto* Hb = static_cast<const uint16_t*>(H);
+  FLCE_TRY(launch(FLCE_K_AUX, prof, s, [&] {
+    flce::colsum_partial_kernel<<<dim3(int(cdiv(D, 256)), flce::kColSplits), dim3(256), 0, s>>>(
+        Hb, y, N, D, d->ignore_index, w.part);
+  }));
+  FLCE_TRY(launch(FLCE_K_AUX, prof, s, [&] {
+    flce::colsum_final_kernel<<<dim3(int(cdiv(D, 256))), dim3(256), 0, s>>>(w.part, D, w.hbar);
+  }));
+  FLCE_TRY(launch(FLCE_K_AUX, prof, s, [&] {
+    flce::vocab_key_kernel<<<dim3(int(cdiv(V, 4))), dim3(256), 0, s>>>(
+        static_cast<const uint16_t*>(W), w.hbar, V, D, w.keys[0]);
+  }));
+  const int* idx_in = nullptr;
+  for (int pass = 0; pass < 4; ++pass) {
+    uint32_t* kin = w.keys[pass & 1];
+    uint32_t* kout = w.keys[(pass + 1) & 1];
+    int* iout = (pass & 1) ? w.vperm : w.idx;
+    FLCE_TRY(launch(FLCE_K_AUX, prof, s, [&] {
+      flce::sort_hist_kernel<<<dim3(p.nsblk), dim3(256), 0, s>>>(kin, V, 8 * pass, p.nsblk, w.hist);
+    }));
+    FLCE_TRY(launch(FLCE_K_AUX, prof, s, [&] {
+      flce::sort_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(w.hist, 256 * p.nsblk);
+    }));
+    FLCE_TRY(launch(FLCE_K_AUX, prof, s, [&] {
+      flce::sort_scatter_kernel<<<dim3(p.nsblk), dim3(256), 0, s>>>(kin, idx_in, V, 8 * pass,
+                                                                     p.nsblk, w.hist, kout, iout);
+    }));
+    idx_in = iout;
+  }
+  return launch(FLCE_K_AUX, prof, s, [&] {
+    flce::invert_perm_kernel<<<dim3(int(cdiv(V, 256))), dim3(256), 0, s>>>(w.vperm, V, w.vinv);
+  });
+}
+
 // One backward launch: grid = g_grad gradient tiles (the first g_long of the
 // contraction with the longer K) + the dZ tiles of `da`.
 template <typename T, bool BF16G>
-void band_kernel(bool filt, bool compact, dim3 grid, hipStream_t s, const flce::GradArgs<T>& ga,
-                 const flce::DzArgs<T>& da, int g_long, int g_grad, int h_first) {
+void band_kernel(bool filt, bool compact, bool sort, dim3 grid, hipStream_t s,
+                 const flce::GradArgs<T>& ga, const flce::DzArgs<T>& da, int g_long, int g_grad,
+                 int h_first) {
   const dim3 block(flce::kThreads);
   if constexpr (sizeof(T) == 2) {
+    if (sort) {   // only with the filter
+      if (compact)
+        flce::bwd_band_kernel<T, true, true, BF16G, true><<<grid, block, 0, s>>>(ga, da, g_long,
+                                                                                 g_grad, h_first);
+      else
+        flce::bwd_band_kernel<T, true, false, BF16G, true><<<grid, block, 0, s>>>(ga, da, g_long,
+                                                                                  g_grad, h_first);
+      return;
+    }
     if (compact) {
       if (filt)
         flce::bwd_band_kernel<T, true, true, BF16G><<<grid, block, 0, s>>>(ga, da, g_long, g_grad,
@@ -367,6 +466,7 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
   const int skip_h = (d->flags & FLCE_FLAG_FILTER_FULL_E) ? 0 : 1;
   const int skip_w = (d->flags & FLCE_FLAG_FILTER_FULL_C) ? 0 : 1;
   const int keep_dropped = skip_h && skip_w ? 0 : 1;
+  if (p.sort) FLCE_TRY(run_sort(d, p, H, W, y, w, prof, s));
   if (w.rowmap)   // dH rows of ignored rows: no tile writes them
     FLCE_TRY(launch(FLCE_K_AUX, prof, s, [&] {
       flce::zero_ignored_rows_kernel<<<dim3(int(cdiv(N, 16))), dim3(256), 0, s>>>(
@@ -379,7 +479,7 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
     return flce::DzArgs<T>{static_cast<const T*>(H), static_cast<const T*>(W), y, lse, dloss_rows,
                            w.hdr, N, D, V, d->ignore_index, d->reduction, d->filter_eps, band,
                            TMv, TNn, reinterpret_cast<T*>(w.dz[buf]), w.flags[buf],
-                           w.flagsT[buf], w.rowmap, keep_dropped};
+                           w.flagsT[buf], w.rowmap, keep_dropped, w.vperm, w.vinv};
   };
   // gradient tiles of band k reading buffer `buf`; g_long, g_grad, h_first out
   auto grad_args = [&](int k, int buf, int& g_long, int& g_grad, int& h_first) {
@@ -398,21 +498,22 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
                              p.bf16g ? nullptr : static_cast<float*>(dW), N, D, V, band, T3n, T2n,
                              Td, bv > 0 ? 1 : 0, bn > 0 ? 1 : 0, skip_h, skip_w, w.rowmap, w.hdr,
                              p.bf16g ? static_cast<uint16_t*>(dH) : nullptr,
-                             p.bf16g ? static_cast<uint16_t*>(dW) : nullptr, w.stage, h_mode};
+                             p.bf16g ? static_cast<uint16_t*>(dW) : nullptr, w.stage, h_mode,
+                             w.vperm};
   };
   if (p.bf16g) {
     if constexpr (sizeof(T) == 2) {
       for (int k = 0; k < nb; ++k) {
         const flce::DzArgs<T> da = dz_args(k, 0);
         FLCE_TRY(launch(FLCE_K_BWD_DZ, prof, s, [&] {
-          band_kernel<T, true>(filt, p.compact, dim3(da.TMv * da.TNn), s, flce::GradArgs<T>{}, da,
-                               0, 0, 1);
+          band_kernel<T, true>(filt, p.compact, p.sort, dim3(da.TMv * da.TNn), s,
+                               flce::GradArgs<T>{}, da, 0, 0, 1);
         }));
         int g_long = 0, g_grad = 0, h_first = 1;
         const flce::GradArgs<T> ga = grad_args(k, 0, g_long, g_grad, h_first);
         FLCE_TRY(launch(FLCE_K_BWD_GRAD, prof, s, [&] {
-          band_kernel<T, true>(filt, p.compact, dim3(g_grad), s, ga, flce::DzArgs<T>{}, g_long,
-                               g_grad, h_first);
+          band_kernel<T, true>(filt, p.compact, p.sort, dim3(g_grad), s, ga, flce::DzArgs<T>{},
+                               g_long, g_grad, h_first);
         }));
       }
       return FLCE_OK;
@@ -430,8 +531,8 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
     if (k > 0) ga = grad_args(k - 1, (k - 1) & 1, g_long, g_grad, h_first);
     const int cls = k == 0 ? FLCE_K_BWD_DZ : (k == nb ? FLCE_K_BWD_GRAD : FLCE_K_BWD_BAND);
     FLCE_TRY(launch(cls, prof, s, [&] {
-      band_kernel<T, false>(filt, p.compact, dim3(g_grad + g_dz), s, ga, da, g_long, g_grad,
-                            h_first);
+      band_kernel<T, false>(filt, p.compact, p.sort, dim3(g_grad + g_dz), s, ga, da, g_long,
+                            g_grad, h_first);
     }));
   }
   return FLCE_OK;
@@ -483,6 +584,7 @@ int flce_plan(const flce_desc* d, flce_plan_info* out) {
   out->tile = flce::kTile;
   out->filter_block = kFilterBlock;
   out->dz_bytes = int64_t(p.NS) * p.VS * p.es;   // one dZ buffer
+  out->vocab_order_offset = p.sort ? int64_t(p.off_vperm) : -1;
   return FLCE_OK;
 }
 

@@ -527,6 +527,8 @@ struct DzArgs {
   uint8_t* flagsT;       // [fcols][frows]
   const int* rowmap;     // row compaction: band rows are positions of rowmap (else rows)
   int keep_dropped;      // store dropped blocks' dZ too (filter on one product only)
+  const int* vperm;      // sorted vocabulary: band position p is vocabulary row vperm[p]
+  const int* vinv;       // and row v sits at position vinv[v] (null: natural order)
 };
 
 // dZ tile t of a band: Z = W_v H_n^T recomputed, G = softmax(Z) - onehot(y),
@@ -555,7 +557,8 @@ __device__ __forceinline__ void dz_tile(const DzArgs<T>& a, int t, char* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  const Operand A{reinterpret_cast<const char*>(W), D, V, D};
+  // vocabulary positions are rows of W, or rows vperm[p] with a sorted vocabulary
+  const Operand A{reinterpret_cast<const char*>(W), D, V, D, a.vperm};
   const Operand B{reinterpret_cast<const char*>(H), D, nval, D, rowmap};
   f32x16 acc[4][4];
   tile_contract<T, false, false>(A, B, v0, n0, D, AllActive{}, acc, lds);
@@ -576,7 +579,7 @@ __device__ __forceinline__ void dz_tile(const DzArgs<T>& a, int t, char* lds) {
     const float gj = reduction == 2 ? (dloss_rows ? dloss_rows[in ? n : 0] : 1.f) : gs;
     g[j] = bad[j] ? __builtin_nanf("") : (valid ? gj : 0.f);
     ml[j] = valid ? lse[n] * kLog2e : INFINITY;       // rows outside the loss get p = 0
-    rel[j] = (valid && !bad[j]) ? (int)(yy - vw) : -1;
+    rel[j] = (valid && !bad[j]) ? (a.vinv ? a.vinv[yy] : (int)yy) - vw : -1;   // target's position
   }
   const int fr0 = (n0 - band.nb0 + wn * 128) >> 6;   // flag row of this wave's first 64 rows
   const int fc0 = (v0 - band.vb0 + wm * 128) >> 6;   // flag column of its first 64 vocab rows
@@ -773,14 +776,16 @@ struct GradArgs {
   uint16_t* dWb;
   float* stage;
   int h_mode;
+  const int* vperm;        // SORT: band vocabulary position p is row vperm[p] of W and dW
 };
 
 // Epilogue of a gradient tile with bf16 in or out: out[r][d] = acc + src[r][d]
 // (src optional) for the tile rows r < rvalid - row0 and d < D.  src rows are
-// the tile's rows; out rows are the same or, with `map`, map[r].  Same
-// two-row-groups-in-flight order as the float epilogue; bf16 values are
-// widened exactly and rounded to nearest even once.
-template <bool SRC_BF16, bool DST_BF16>
+// the tile's rows (SRC_MAPPED: map[r] like the out rows); out rows are the
+// same or, with `map`, map[r].  Same two-row-groups-in-flight order as the
+// float epilogue; bf16 values are widened exactly and rounded to nearest even
+// once.
+template <bool SRC_BF16, bool DST_BF16, bool SRC_MAPPED = false>
 __device__ __forceinline__ void grad_epilogue_cvt(const f32x16 (&acc)[4][4], bool src_on,
                                                   __amdgpu_buffer_rsrc_t rsS,
                                                   __amdgpu_buffer_rsrc_t rsD, const int* map,
@@ -796,7 +801,7 @@ __device__ __forceinline__ void grad_epilogue_cvt(const f32x16 (&acc)[4][4], boo
       for (int q = 0; q < 4; ++q) {
         const int d = dw + 32 * i + 8 * q;
         const bool ok = rok && d < D;
-        os[i][q] = ok ? (uint32_t)(((int64_t)lr * D + d) * SES) : kOob;
+        os[i][q] = ok ? (uint32_t)(((SRC_MAPPED ? orow : (int64_t)lr) * D + d) * SES) : kOob;
         od[i][q] = ok ? (uint32_t)((orow * D + d) * DES) : kOob;
       }
   };
@@ -861,7 +866,10 @@ __device__ __forceinline__ void grad_epilogue_cvt(const f32x16 (&acc)[4][4], boo
 // not made): dH^T tiles past them exit, their rows are scattered through the
 // map, and dW^T contracts over them only, gathering H's rows through an LDS
 // copy of the map.
-template <typename T, bool FILTER, bool COMPACT = false, bool BF16G = false>
+// SORT: the band's vocabulary positions are rows vperm[p]: dH^T gathers W's
+// k rows through an LDS copy of the band's part of vperm, dW^T rows are
+// scattered through it.
+template <typename T, bool FILTER, bool COMPACT = false, bool BF16G = false, bool SORT = false>
 __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int local, char* lds) {
   const T* __restrict__ H = a.H;
   const T* __restrict__ W = a.W;
@@ -886,13 +894,24 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
     out = dH + (int64_t)band.nb0 * D;
     rvalid = COMPACT ? nrows : band.ns_cur;
     beta = beta_h;
-    const Operand A{reinterpret_cast<const char*>(W + (int64_t)band.vb0 * D), D, D, band.vs_cur};
     const int kpad = (band.vs_cur + kTile - 1) / kTile * kTile;
     const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T3n * kTile, kpad};
-    if constexpr (FILTER) {
+    if constexpr (SORT) {
+      static_assert(FILTER, "the vocabulary order only serves the filter");
+      char* table = lds + kDmaLdsBytes + 256;
+      const int half = band.fcols * kFilterHalfPerBlock;   // VS / 2 entries per parity
+      gather_table(table, a.vperm + band.vb0, band.vs_cur, half);
+      const Operand A{reinterpret_cast<const char*>(W), D, D, band.vs_cur,
+                      reinterpret_cast<const int*>(table), half};
+      const SkipRowsOfFlags<step_k<T>()> act{flagsT + tr * 4, band.frows, !a.skip_h};
+      tile_contract<T, true, false, SkipRowsOfFlags<step_k<T>()>, true>(
+          A, B, td * kTile, tr * kTile, band.vs_cur, act, acc, lds);
+    } else if constexpr (FILTER) {
+      const Operand A{reinterpret_cast<const char*>(W + (int64_t)band.vb0 * D), D, D, band.vs_cur};
       const SkipRowsOfFlags<step_k<T>()> act{flagsT + tr * 4, band.frows, !a.skip_h};
       tile_contract<T, true, false>(A, B, td * kTile, tr * kTile, band.vs_cur, act, acc, lds);
     } else {
+      const Operand A{reinterpret_cast<const char*>(W + (int64_t)band.vb0 * D), D, D, band.vs_cur};
       tile_contract<T, true, false>(A, B, td * kTile, tr * kTile, band.vs_cur, AllActive{}, acc,
                                     lds);
     }
@@ -953,23 +972,32 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
                                        rvalid, D, dw, lw);
       }
     } else {
-      const auto rs = make_rsrc(
-          reinterpret_cast<const char*>(a.dWb + ((int64_t)band.vb0 + row0) * D));
-      grad_epilogue_cvt<true, true>(acc, beta_w != 0, rs, rs, nullptr, row0, rvalid, D, dw, lw);
+      if constexpr (SORT) {   // rows scattered: offsets from the start of dW (V D 4 < 2^31)
+        const auto rs = make_rsrc(reinterpret_cast<const char*>(a.dWb));
+        grad_epilogue_cvt<true, true, true>(acc, beta_w != 0, rs, rs, a.vperm + band.vb0 + row0,
+                                            row0, rvalid, D, dw, lw);
+      } else {
+        const auto rs = make_rsrc(
+            reinterpret_cast<const char*>(a.dWb + ((int64_t)band.vb0 + row0) * D));
+        grad_epilogue_cvt<true, true>(acc, beta_w != 0, rs, rs, nullptr, row0, rvalid, D, dw, lw);
+      }
     }
     return;
   }
-  // with compaction the dH^T tile's rows are scattered through the map:
-  // offsets from the start of dH (below 2^31 by the planner's check)
-  const bool scatter = COMPACT && is_h;
+  // with compaction the dH^T tile's rows are scattered through the row map,
+  // with a sorted vocabulary the dW^T tile's rows through vperm: offsets from
+  // the start of dH / dW (below 2^31 by the planner's checks)
+  const int* smap = is_h ? (COMPACT ? a.rowmap + band.nb0 + row0 : nullptr)
+                         : (SORT ? a.vperm + band.vb0 + row0 : nullptr);
+  const bool scatter = (COMPACT && is_h) || (SORT && !is_h);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(
-      scatter ? dH : out + (int64_t)row0 * D));
+      scatter ? (is_h ? dH : dW) : out + (int64_t)row0 * D));
   // Two row groups in flight: the loads of group j + 1 (and j + 2) are out
   // while group j is added and stored.
   auto offsets = [&](int j, uint32_t (&off)[4][4]) {
     const int lr = lw + 32 * j;
     const bool rok = row0 + lr < rvalid;
-    const int64_t orow = scatter ? (rok ? (int64_t)a.rowmap[band.nb0 + row0 + lr] : 0) : lr;
+    const int64_t orow = scatter ? (rok ? (int64_t)smap[lr] : 0) : lr;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1022,11 +1050,11 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
 // [g_grad, G) dZ tiles.
 constexpr int kBandLdsCompact = kDmaLdsBytes + 256 + kGatherTableBytes;   // slots, line touch, map
 
-template <typename T, bool FILTER, bool COMPACT, bool BF16G = false>
+template <typename T, bool FILTER, bool COMPACT, bool BF16G = false, bool SORT = false>
 __global__ void __launch_bounds__(kThreads, 1)
 bwd_band_kernel(GradArgs<T> ga, DzArgs<T> da, int g_long, int g_grad, int h_first) {
   __shared__ __attribute__((aligned(1024))) char
-      lds[COMPACT && kBandLdsCompact > kLdsBytes ? kBandLdsCompact : kLdsBytes];
+      lds[(COMPACT || SORT) && kBandLdsCompact > kLdsBytes ? kBandLdsCompact : kLdsBytes];
   const int t = xcd_remap_kinds(blockIdx.x, gridDim.x, g_long, g_grad);
   if (t >= g_grad) {
     dz_tile<T>(da, t - g_grad, lds);
@@ -1035,7 +1063,7 @@ bwd_band_kernel(GradArgs<T> ga, DzArgs<T> da, int g_long, int g_grad, int h_firs
   const int T3 = ga.Td * ga.T3n;   // dH^T tiles
   const bool is_h = h_first ? t < T3 : t >= g_long;
   const int local = h_first ? (is_h ? t : t - T3) : (is_h ? t - g_long : t);
-  grad_tile<T, FILTER, COMPACT, BF16G>(ga, is_h, local, lds);
+  grad_tile<T, FILTER, COMPACT, BF16G, SORT>(ga, is_h, local, lds);
 }
 
 }  // namespace flce

@@ -42,7 +42,7 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(_abi.FlceDesc) == 3 * 8 + 2 * 4 + 8 + 4 + 4 + 8
     assert _abi.FlceDesc.ignore_index.offset == 32
     assert _abi.FlceDesc.ws_budget_bytes.offset == 48
-    assert ctypes.sizeof(_abi.FlcePlanInfo) == 8 + 8 * 4 + 8
+    assert ctypes.sizeof(_abi.FlcePlanInfo) == 8 + 8 * 4 + 8 + 8
 
 
 def test_strerror_covers_codes():
@@ -70,11 +70,24 @@ def test_invalid_dtype_reduction_flags_eps():
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_DTYPE
     d = L.make_desc(8, 64, 10, reduction=5)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
-    d = L.make_desc(8, 64, 10, flags=32)
+    d = L.make_desc(8, 64, 10, flags=64)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
     # a filter on one product: C or E, not both
     d = L.make_desc(8, 64, 10, flags=_abi.FLCE_FLAG_FILTER_FULL_C | _abi.FLCE_FLAG_FILTER_FULL_E)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    # vocabulary sorting: bf16, 32-bit offsets of gathered W / scattered dW rows
+    S = _abi.FLCE_FLAG_SORT_VOCAB
+    d = L.make_desc(8, 64, 10, dtype=torch.float32, filter_eps=2.0 ** -12, flags=S)
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    d = L.make_desc(8, 4096, 131072, filter_eps=2.0 ** -12, flags=S)
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
+    d = L.make_desc(8192, 2048, 151552, filter_eps=2.0 ** -12, flags=S)
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_OK
+    assert info.band_vocab <= 4096 and info.vocab_order_offset > 0
+    assert info.vocab_order_offset + 8 * 151552 <= info.ws_bytes <= 64 << 20
+    d = L.make_desc(8192, 2048, 151552, flags=S)          # no filter: nothing to sort for
+    assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_OK
+    assert info.vocab_order_offset == -1
     for f in (_abi.FLCE_FLAG_FILTER_FULL_C, _abi.FLCE_FLAG_FILTER_FULL_E):
         d = L.make_desc(8, 64, 10, filter_eps=2.0 ** -12, flags=f)
         assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_OK

@@ -173,6 +173,9 @@ def parse():
     p.add_argument("--filter-eps", type=float, default=0.0)
     p.add_argument("--compact-ignored", action="store_true",
                    help="remove rows whose target is ignore_index before every contraction")
+    p.add_argument("--sort-vocab", action="store_true",
+                   help="filter blocks over the vocabulary sorted by average logit "
+                        "(FLCE_FLAG_SORT_VOCAB; needs --filter-eps)")
     p.add_argument("--bf16-grads", action="store_true",
                    help="dH and dW written in bf16 (FLCE_FLAG_BF16_GRADS)")
     p.add_argument("--cpu-rows", type=int, default=8192,
@@ -272,6 +275,8 @@ def main():
     flags0 = L.FLCE_FLAG_COMPACT_IGNORED if args.compact_ignored else 0
     if args.bf16_grads:
         flags0 |= L.FLCE_FLAG_BF16_GRADS
+    if args.sort_vocab:
+        flags0 |= L.FLCE_FLAG_SORT_VOCAB
     gdt = torch.bfloat16 if args.bf16_grads else torch.float32
     plan = L.flce_plan(N, D, V, dtype=Hd.dtype, reduction=wl.reduction,
                        filter_eps=args.filter_eps, flags=flags0)
@@ -350,7 +355,7 @@ def main():
         achieved = per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
         traffic = None
         if (dom == "bwd_band" and args.workload == "large_vocab" and args.filter_eps == 0.0
-                and not args.compact_ignored and not args.bf16_grads):
+                and not args.compact_ignored and not args.bf16_grads and not args.sort_vocab):
             traffic = stored_traffic()
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                     "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -371,6 +376,7 @@ def main():
                    "ignore_frac": wl.ignore_frac, "filter_eps": args.filter_eps,
                    "compact_ignored": bool(args.compact_ignored),
                    "grad_dtype": "bf16" if args.bf16_grads else "f32",
+                   "sort_vocab": bool(args.sort_vocab),
                    "parallelism": "single GPU"},
         "mfma_util": round(tflops / peak, 4), "tflops_counted_8ndv": round(tflops, 1),
         "ms_median": round(float(np.median(per)), 4), "ms_p95": round(float(np.percentile(per, 95)), 4),

@@ -129,6 +129,47 @@ def test_large_vocab_filter(large_vocab):
 
 
 @pytest.mark.timeout(900)
+def test_large_vocab_sorted_filter(large_vocab):
+    """Filter over the sorted vocabulary at full size.  The order is decided
+    on float32 keys, so what is checked is what is unique: a permutation,
+    sorted by the fp64 keys up to ten times the error of a float32
+    re-summation of them; the loss untouched by the filter; the properties
+    that hold under the filter; the error against the exact gradients
+    reported."""
+    H, W, y, Hd, Wd, yd, lse_ref = large_vocab
+    S = L.FLCE_FLAG_SORT_VOCAB
+    N, D = H.shape
+    V = W.shape[0]
+    plan = L.flce_plan(N, D, V, filter_eps=EPS, flags=S)
+    assert plan["ws_bytes"] <= 64 << 20
+    ws = L.Workspace(plan["ws_bytes"], DEV)
+    loss, rows, lse, dH, dW = L.flce_fused_fwd_bwd(Hd, Wd, yd, filter_eps=EPS, flags=S, ws=ws)
+    torch.cuda.synchronize()
+    off = plan["vocab_order_offset"]
+    order = ws.buf[off:off + 4 * V].view(torch.int32).cpu().numpy().astype(np.int64)
+    assert np.array_equal(np.sort(order), np.arange(V))
+    valid = (y != -100).numpy()
+    hsum = np64(H)[valid].sum(0)
+    key = np64(W) @ hsum                       # sum over kept rows of each entry's logits
+    h32 = H.float()[torch.from_numpy(valid)].sum(0)
+    key32 = (W.float() @ h32).double().numpy()
+    bound = 10 * float(np.abs(key32 - key).max())
+    step = key[order][:-1] - key[order][1:]
+    yn = y.numpy()
+    g = O.row_scale(yn, V, -100, "mean")
+    rs = _sample(N, 48, 31)
+    vs = _sample(V, 48, 32, extra=yn[np.nonzero(valid)[0][:8]].tolist())
+    vals = dict(worst_step=float(step.min()), bound=bound,
+                loss=rel(loss.item(), float(np64(L.flce_forward(Hd, Wd, yd)[0])[0])),
+                dH_vs_exact=max_abs_rel(dH[rs], O.dH_rows(H, W, y, lse_ref, g, rs)),
+                dW_vs_exact=max_abs_rel(dW[vs], O.dW_rows(H, W, y, lse_ref, g, vs)))
+    report("large_vocab_sorted_filter", **vals)
+    assert step.min() >= -bound
+    assert vals["loss"] == 0.0
+    _properties("large_vocab_sorted_filter", H, W, y, dH.cpu(), dW.cpu(), filtered=True)
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["wide", "wide_peaked"])
 def test_wide_sampled(name):
     H, W, y = fi.make(name)

@@ -245,14 +245,27 @@ lse_combine_kernel(const float* __restrict__ part_m, const float* __restrict__ p
   const bool live = nl < ns && (!rowmap || nb0 + nl < hdr->nvalid);
   float M = -INFINITY, S = 0.f;
   if (live) {
-    for (int k = sl; k < Tv; k += 16) {
-      const float m = part_m[(int64_t)k * ns + nl], sk = part_s[(int64_t)k * ns + nl];
-      if (m == -INFINITY) continue;
-      if (m <= M) {
-        S += sk * fast_exp2((m - M) * kLog2e);
-      } else {
-        S = S * fast_exp2((M - m) * kLog2e) + sk;   // M = -inf: S = 0 * 0 + sk
-        M = m;
+    // partials k = sl, sl + 16, ... in increasing order; the loads of eight
+    // of them go out together, ahead of the dependent merges
+    constexpr int kBatch = 8;
+    for (int k0 = sl; k0 < Tv; k0 += 16 * kBatch) {
+      float mb[kBatch], sb[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int k = k0 + 16 * u;
+        mb[u] = k < Tv ? part_m[(int64_t)k * ns + nl] : -INFINITY;
+        sb[u] = k < Tv ? part_s[(int64_t)k * ns + nl] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float m = mb[u], sk = sb[u];
+        if (m == -INFINITY) continue;
+        if (m <= M) {
+          S += sk * fast_exp2((m - M) * kLog2e);
+        } else {
+          S = S * fast_exp2((M - m) * kLog2e) + sk;   // M = -inf: S = 0 * 0 + sk
+          M = m;
+        }
       }
     }
   }

@@ -38,6 +38,10 @@
  *     Every entry point clears the status word when it starts.
  *   - Results are deterministic: no floating-point atomics, fixed reduction
  *     orders; two calls with the same inputs give the same bits.
+ *   - The library keeps no state between calls other than the profiling
+ *     record (guarded by a mutex), so calls from several host threads are
+ *     safe; two calls whose work overlaps on the device must not share a
+ *     workspace (the workspace carries each call's intermediate data).
  */
 #ifndef FLCE_H
 #define FLCE_H

@@ -28,3 +28,14 @@ def rel(got, ref) -> float:
 def report(name, **vals):
     txt = " ".join(f"{k}={v:.3e}" if isinstance(v, float) else f"{k}={v}" for k, v in vals.items())
     print(f"[{name}] {txt}", flush=True)
+
+
+def norm_cos(got, ref):
+    """(relative error of the Frobenius norm, cosine of the angle) between a
+    gradient and its reference, the two summary figures the PyTorch 2.13
+    chapter lists for comparing gradients."""
+    g, r = np64(got).ravel(), np64(ref).ravel()
+    ng, nr = float(np.linalg.norm(g)), float(np.linalg.norm(r))
+    if nr == 0.0:
+        return (ng, 1.0 if ng == 0.0 else 0.0)
+    return (abs(ng - nr) / nr, float(g @ r) / (ng * nr) if ng > 0 else 0.0)

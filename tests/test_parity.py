@@ -10,7 +10,7 @@ import torch
 import flce_inputs as fi
 import linear_cross_entropy_online_amd as L
 from oracle import flce_oracle as O
-from tests.gpu_util import TOL, max_abs_rel, np64, rel, report
+from tests.gpu_util import TOL, max_abs_rel, norm_cos, np64, rel, report
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -31,12 +31,16 @@ def _check_against_oracle(name, H, W, y, out, ref, dt, reduction="mean", grads=T
     if grads:
         vals["dH"] = max_abs_rel(out[3], ref["dH"])
         vals["dW"] = max_abs_rel(out[4], ref["dW"])
+        vals["dH_norm"], vals["dH_cos"] = norm_cos(out[3], ref["dH"])
+        vals["dW_norm"], vals["dW_cos"] = norm_cos(out[4], ref["dW"])
     report(name, **vals)
     assert e_lse <= tol["loss"] and e_rows <= tol["loss"]
     if reduction != "none":
         assert vals["loss"] <= tol["loss"]
     if grads:
         assert vals["dH"] <= tol["grad"] and vals["dW"] <= tol["grad"]
+        assert vals["dH_norm"] <= tol["grad"] and vals["dW_norm"] <= tol["grad"]
+        assert vals["dH_cos"] >= 1 - tol["grad"] ** 2 and vals["dW_cos"] >= 1 - tol["grad"] ** 2
         for t in out[3:5]:
             assert torch.isfinite(t).all()
 

@@ -31,16 +31,29 @@ TRAFFIC_FILE = os.path.join(PROFILES, "bwd_band_8192x2048x151552_hbm_traffic.txt
 DOMINANT = "bwd_band_kernel<unsigned short, false, false, false, false>"   # the backward launch of the default run
 
 
+def _code_only(text):
+    """The source without comments and blank lines (comments do not change
+    the compiled kernels)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = []
+    for line in text.splitlines():
+        line = re.sub(r"//.*$", "", line).rstrip()
+        if line:
+            out.append(line)
+    return "\n".join(out)
+
+
 def source_hash():
-    """sha256 over the kernel sources: a stored traffic figure holds only for
-    the kernels it was measured on."""
+    """sha256 over the code of the kernel sources (comments stripped): a
+    stored traffic figure holds only for the kernels it was measured on."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(SRC_DIR)):
         if name.endswith((".hpp", ".hip")):
             h.update(name.encode())
-            with open(os.path.join(SRC_DIR, name), "rb") as f:
-                h.update(f.read())
+            with open(os.path.join(SRC_DIR, name), encoding="utf-8") as f:
+                h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 

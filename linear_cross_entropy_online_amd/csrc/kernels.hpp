@@ -11,14 +11,18 @@
 //                       paper's spin-locked log-add-exp), plus per-block sums.
 //   finalize_kernel     fixed-order scalar loss, valid-row count, row scale.
 //   bwd_prep_kernel     the same count / scale for a standalone backward.
-//   bwd_dz_kernel       recomputes a logits tile and writes
+//   bwd_band_kernel     one backward launch of two tile kinds:
+//     dz_tile           recomputes a logits tile and writes
 //                       dZ = g_n (softmax - onehot) for one band into the
 //                       workspace, with 64x64 filter flags (CCE Alg. 4, first
-//                       half; gradient filtering of Sec. 4.3).
-//   bwd_grad_kernel     one launch holding both band contractions:
-//                       dH[band rows] (+)= dZ W[band vocab] and
-//                       dW[band vocab] (+)= dZ^T H[band rows] (Alg. 4, second
-//                       half, done as two ordinary MFMA GEMMs without locks).
+//                       half; gradient filtering of Sec. 4.3);
+//     grad_tile         the band contractions dH[band rows] (+)= dZ W[band
+//                       vocab] and dW[band vocab] (+)= dZ^T H[band rows]
+//                       (Alg. 4, second half, done as two ordinary MFMA GEMMs
+//                       without locks), float or bf16 outputs.
+//   compact_*, zero_ignored_rows_kernel   ignored-row compaction (CCE App. B).
+//   fill / scale / clear kernels          small helpers.
+// vocab_sort.hpp holds the kernels of the sorted vocabulary (CCE Sec. 4.3).
 #pragma once
 
 #include "tile_dma.hpp"

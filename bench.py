@@ -136,6 +136,42 @@ def summarize_pmc(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_bytes,
     print("\n".join(lines))
 
 
+def summarize_clock(d, out, cmds):
+    """Average GRBM_GUI_ACTIVE cycles per microsecond of each kernel (a
+    rocprofv3 --pmc run), divided by the 8 XCDs whose counters rocprofv3 sums:
+    the clock the kernel ran at, for kernels long enough that the counting
+    window is the kernel."""
+    import collections
+    per = collections.defaultdict(lambda: [0.0, 0.0, 0])
+    seen = {}
+    for r in _pmc_rows(d):
+        if r["Counter_Name"] != "GRBM_GUI_ACTIVE":
+            continue
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        key = (name, r["Dispatch_Id"])
+        if key in seen:
+            seen[key][0] += float(r["Counter_Value"])
+            continue
+        seen[key] = [float(r["Counter_Value"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])]
+    for (name, _), (cyc, ns) in seen.items():
+        p = per[name]
+        p[0] += cyc
+        p[1] += ns
+        p[2] += 1
+    lines = ["# Clock of each kernel: GRBM_GUI_ACTIVE cycles (summed by rocprofv3 over the",
+             "# 8 XCDs) / kernel duration / 8, 8192 x 2048 x 151552 bf16 fused step.",
+             "# Commands (run from the repository root on one MI355X):"]
+    lines += [f"#   {c}" for c in cmds]
+    lines += ["", "| kernel | dispatches | avg us | GHz per XCD |", "|---|---|---|---|"]
+    for name, (cyc, ns, n) in sorted(per.items(), key=lambda kv: -kv[1][1]):
+        us = ns / n / 1e3
+        lines.append(f"| `{name}` | {n} | {us:.1f} | {cyc / ns / 8:.2f}"
+                     + (" (window longer than the kernel)" if us < 50 else "") + " |")
+    with open(out, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_trace(d, out, title, cmd, bench_json=None):
     import csv
     stats = trace = None
@@ -200,6 +236,7 @@ def parse():
     p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR",
                                                          "CAL_WRITE_DIR"))
     p.add_argument("--summarize-trace", metavar="DIR")
+    p.add_argument("--summarize-clock", metavar="DIR")
     p.add_argument("--cal-bytes", type=int, default=1 << 30)
     p.add_argument("--out")
     p.add_argument("--title", default="")
@@ -260,6 +297,9 @@ def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.cal_bytes, args.out, args.cmd)
+        return
+    if args.summarize_clock:
+        summarize_clock(args.summarize_clock, args.out, args.cmd)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, args.title, " ".join(args.cmd),

@@ -184,8 +184,8 @@ int flce_plan(const flce_desc* d, flce_plan_info* out);
  * loss may be NULL iff reduction == FLCE_NONE.  The logits are produced one
  * 256 x 256 tile per workgroup in registers and reduced to a per-(row,
  * vocabulary tile) max and sum-exp; a second pass merges a row's partials in
- * a fixed order (CCE Alg. 2 without the lock).  The target logit is picked
- * from the same accumulators (CCE Alg. 1). */
+ * a fixed order (CCE Alg. 2 without the lock).  The target logit of each row
+ * is its own pass, a dot product of the row with W's target row (CCE Alg. 1). */
 int flce_forward(const flce_desc* d, const void* H, const void* W, const int64_t* y,
                  float* loss_rows, float* lse, float* loss,
                  void* ws, size_t ws_bytes, hipStream_t stream);

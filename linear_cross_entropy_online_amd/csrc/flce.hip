@@ -2,6 +2,7 @@
 // cross-entropy library (declared in include/flce.h).
 //
 // Launch sequence of one fused call on the caller's stream:
+//   target_logit_kernel  z_y of every row (one wave per row)
 //   for each band of NF token rows:
 //     fwd_lse_kernel     grid = ceil(V/256) x ceil(NF/256) logits tiles
 //     lse_combine_kernel grid = ceil(NF/256)
@@ -331,6 +332,10 @@ template <typename T>
 int run_forward(const flce_desc* d, const Plan& p, const void* H, const void* W, const int64_t* y,
                 float* loss_rows, float* lse, float* loss, const Ws& w, bool prof, hipStream_t s) {
   const int N = int(p.N), D = int(p.D), V = int(p.V);
+  FLCE_TRY(launch(FLCE_K_AUX, prof, s, [&] {
+    flce::target_logit_kernel<T><<<dim3(int(cdiv(N, 4))), dim3(256), 0, s>>>(
+        static_cast<const T*>(H), static_cast<const T*>(W), y, N, D, V, w.rowmap, w.zy);
+  }));
   for (int bf = 0; bf < p.nbf; ++bf) {
     const int nb0 = bf * p.NF;
     const int ns = int(std::min<int64_t>(p.NF, p.N - nb0));
@@ -339,8 +344,8 @@ int run_forward(const flce_desc* d, const Plan& p, const void* H, const void* W,
     float* ps = w.pm + size_t(p.Tv) * ns;
     FLCE_TRY(launch(FLCE_K_FWD_LSE, prof, s, [&] {
       flce::fwd_lse_kernel<T><<<dim3(p.Tv * TNn), dim3(flce::kThreads), 0, s>>>(
-          static_cast<const T*>(H), static_cast<const T*>(W), y, N, D, V, d->ignore_index, nb0,
-          ns, p.Tv, TNn, pm, ps, w.zy, w.hdr, w.rowmap);
+          static_cast<const T*>(H), static_cast<const T*>(W), N, D, V, nb0, ns, p.Tv, TNn, pm, ps,
+          w.hdr, w.rowmap);
     }));
     FLCE_TRY(launch(FLCE_K_LSE_COMBINE, prof, s, [&] {
       flce::lse_combine_kernel<<<dim3(int(cdiv(ns, flce::kCombineRows))), dim3(256), 0, s>>>(

@@ -1,11 +1,11 @@
 // kernels.hpp -- device kernels of the fused LM-head + cross-entropy path.
 //
+//   target_logit_kernel z_y = H_n . W[y_n] per row (CCE, arXiv 2411.09009,
+//                       Sec. 4.1 / Alg. 1, the indexed matrix multiplication).
 //   fwd_lse_kernel      Z tile = W_v H_n^T on MFMA; online max / sum-exp per
-//                       token row over this workgroup's vocabulary range; the
-//                       target logit is picked from the same accumulators.
-//                       (CCE, arXiv 2411.09009, Sec. 4.2 / Alg. 2 for the
-//                       blockwise log-sum-exp, Sec. 4.1 / Alg. 1 for the
-//                       indexed logit; online normaliser of Sec. 2.)
+//                       token row over this workgroup's vocabulary range
+//                       (Sec. 4.2 / Alg. 2 for the blockwise log-sum-exp;
+//                       online normaliser of Sec. 2).
 //   lse_combine_kernel  merges the per-split (max, sum) partials of a row in a
 //                       fixed order into LSE and the row loss (replaces the
 //                       paper's spin-locked log-add-exp), plus per-block sums.
@@ -70,75 +70,45 @@ __device__ __forceinline__ void tile_contract(const Operand& A, const Operand& B
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Sets rows >= V of the wave's 128-row block to `val` (block starts at vw).
-__device__ __forceinline__ void mask_rows(f32x16 (&acc)[4][4], int vw, int V, int lane, float val) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (vw + acc_row(i, r, lane) >= V)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j][r] = val;
-}
-
-// sum over this lane's 64 values of column block j of 2^(z log2e - ml)
-template <int J>
-__device__ __forceinline__ float col_expsum(const f32x16 (&acc)[4][4], float ml) {
-  float s4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s4[i] += fast_exp2(fmaf(acc[i][J][r], kLog2e, -ml));
-  return (s4[0] + s4[1]) + (s4[2] + s4[3]);
-}
-
-// acc[i][j][r] for the register holding wave-block row `rel` (0..127), where
-// rel = 32 i + 8 (r >> 2) + 4 half + (r & 3): a select tree on the bits of rel
-// (valid in the lane whose half matches (rel >> 2) & 1).
-template <int J>
-__device__ __forceinline__ float pick_row(const f32x16 (&acc)[4][4], int rel) {
-  const int i = rel >> 5, q = (rel >> 3) & 3, e = rel & 3;
-  float t[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r)
-    t[r] = i == 0 ? acc[0][J][r] : i == 1 ? acc[1][J][r] : i == 2 ? acc[2][J][r] : acc[3][J][r];
-  float u[4];
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-    u[x] = q == 0 ? t[x] : q == 1 ? t[4 + x] : q == 2 ? t[8 + x] : t[12 + x];
-  return e == 0 ? u[0] : e == 1 ? u[1] : e == 2 ? u[2] : u[3];
-}
-
 // Max and sum-exp of one 32-column block (token rows) over this lane's 64
-// logits of the tile, and the target pick.
-template <int J>
-__device__ __forceinline__ void fwd_column(const f32x16 (&acc)[4][4], float& m, float& s, int rel,
-                                           int lane, float* zy_col) {
+// logits of the tile; MASKED: rows of the wave block at or past `lim`
+// (V - first row of the block) are left out (last vocabulary tile).
+template <int J, bool MASKED>
+__device__ __forceinline__ void fwd_column(const f32x16 (&acc)[4][4], float& m, float& s, int lim,
+                                           int lane) {
+  auto val = [&](int i, int r) {
+    return !MASKED || acc_row(i, r, lane) < lim ? acc[i][J][r] : -INFINITY;
+  };
   float tmax = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[i][J][r]);
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, val(i, r));
   m = tmax;
-  s = tmax == -INFINITY ? 0.f : col_expsum<J>(acc, tmax * kLog2e);
-  const bool hit = (unsigned)rel < 128u;
-  if (__any(hit)) {
-    const float z = pick_row<J>(acc, rel & 127);
-    if (hit && ((rel >> 2) & 1) == (lane >> 5)) *zy_col = z;
+  if (tmax == -INFINITY) {
+    s = 0.f;
+    return;
   }
+  const float ml = tmax * kLog2e;
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s4[i] += fast_exp2(fmaf(val(i, r), kLog2e, -ml));
+  s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
 }
 
 // ------------------------------------------------------------- forward ----
 // One 256 (vocabulary) x 256 (token rows) logits tile per workgroup, for the
 // token rows [nb0, nb0 + ns) of a band: Z = W_v H_n^T stays in registers; the
 // tile's per-row max m and sum s = sum_v exp(Z - m) go to
-// part_m / part_s [vocab tile][row of the band], and the target logit of a
-// row whose target lies in the tile goes to zy[row].
+// part_m / part_s [vocab tile][row of the band].  (The target logits come
+// from target_logit_kernel.)
 template <typename T>
 __global__ void __launch_bounds__(kThreads, 1)
-fwd_lse_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* __restrict__ y,
-               int N, int D, int V, int64_t ignore, int nb0, int ns, int TMv, int TNn,
-               float* __restrict__ part_m, float* __restrict__ part_s, float* __restrict__ zy,
+fwd_lse_kernel(const T* __restrict__ H, const T* __restrict__ W,
+               int N, int D, int V, int nb0, int ns, int TMv, int TNn,
+               float* __restrict__ part_m, float* __restrict__ part_s,
                Header* __restrict__ hdr, const int* __restrict__ rowmap) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   if (nb0 == 0 && blockIdx.x == 0 && threadIdx.x == 0) hdr->status = 0;   // start of a forward
@@ -158,21 +128,19 @@ fwd_lse_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* 
   tile_contract<T, false, false>(A, B, v0, n0, D, AllActive{}, acc, lds);
 
   const int vw = v0 + wm * 128;  // first vocabulary row of this wave's block
-  int rel[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = n0 + wn * 128 + j * 32 + (lane & 31);
-    const int n = c < nval ? (rowmap ? rowmap[c] : c) : -1;
-    const int64_t yy = n >= 0 ? y[n] : ignore;
-    rel[j] = (yy >= 0 && yy < V) ? (int)(yy - vw) : -1;
-  }
-  if (vw + 128 > V) mask_rows(acc, vw, V, lane, -INFINITY);   // last vocabulary tile
   float m[4], s[4];
-  float* zc = zy + n0 + wn * 128 + (lane & 31);
-  fwd_column<0>(acc, m[0], s[0], rel[0], lane, zc);
-  fwd_column<1>(acc, m[1], s[1], rel[1], lane, zc + 32);
-  fwd_column<2>(acc, m[2], s[2], rel[2], lane, zc + 64);
-  fwd_column<3>(acc, m[3], s[3], rel[3], lane, zc + 96);
+  if (vw + 128 > V) {   // last vocabulary tile: rows past V are left out
+    const int lim = V - vw;
+    fwd_column<0, true>(acc, m[0], s[0], lim, lane);
+    fwd_column<1, true>(acc, m[1], s[1], lim, lane);
+    fwd_column<2, true>(acc, m[2], s[2], lim, lane);
+    fwd_column<3, true>(acc, m[3], s[3], lim, lane);
+  } else {
+    fwd_column<0, false>(acc, m[0], s[0], 0, lane);
+    fwd_column<1, false>(acc, m[1], s[1], 0, lane);
+    fwd_column<2, false>(acc, m[2], s[2], 0, lane);
+    fwd_column<3, false>(acc, m[3], s[3], 0, lane);
+  }
 
   // merge the two lanes holding one token column, then the two waves
   float* red = reinterpret_cast<float*>(lds);
@@ -208,6 +176,52 @@ fwd_lse_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* 
       }
     }
   }
+}
+
+// Target logits z_y of positions [0, npos): z[pos] = H[n] . W[y_n] for row n
+// = pos (rowmap[pos] with compaction) when y_n is a vocabulary row (CCE
+// Sec. 4.1, Alg. 1: the indexed matrix multiplication as its own pass).  One
+// wave per position, 4 per block: lane L takes d = E L + 64 E i (E = 8 bf16
+// or 4 float per 16-byte load), fp32 products summed in a fixed order, then
+// a fixed xor butterfly over the lanes.  D % 8 == 0, rows 16-byte aligned.
+template <typename T>
+__global__ void __launch_bounds__(256)
+target_logit_kernel(const T* __restrict__ H, const T* __restrict__ W, const int64_t* __restrict__ y,
+                    int npos, int D, int V, const int* __restrict__ rowmap, float* __restrict__ zy) {
+  constexpr int E = 16 / sizeof(T);
+  const int pos = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (pos >= npos) return;
+  const int n = rowmap ? rowmap[pos] : pos;
+  const int64_t yy = y[n];
+  if (yy < 0 || yy >= V) return;   // ignored or invalid target: z is not used
+  const T* h = H + (int64_t)n * D;
+  const T* w = W + yy * D;
+  float acc = 0.f;
+  for (int d = lane * E; d < D; d += 64 * E) {
+    if constexpr (sizeof(T) == 2) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(h + d);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(w + d);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(__builtin_bit_cast(float, a[e] << 16), __builtin_bit_cast(float, b[e] << 16), acc);
+        acc = fmaf(__builtin_bit_cast(float, a[e] & 0xffff0000u),
+                   __builtin_bit_cast(float, b[e] & 0xffff0000u), acc);
+      }
+    } else {
+      // float rows are loaded as float vectors (an integer-vector load
+      // reinterpreted element by element was miscompiled with packed fp32
+      // codegen disabled: overlapping load registers, one product repeated)
+      const f32x4 a = *reinterpret_cast<const f32x4*>(h + d);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(w + d);
+      acc = fmaf(a[0], b[0], acc);
+      acc = fmaf(a[1], b[1], acc);
+      acc = fmaf(a[2], b[2], acc);
+      acc = fmaf(a[3], b[3], acc);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) zy[pos] = acc;
 }
 
 // Fixed-order block reduction of (double sum, int count) over 256 threads.

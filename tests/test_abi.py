@@ -212,3 +212,54 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_abi, "LIB_PATH", "/nonexistent/libflce.so")
     with pytest.raises(ImportError):
         _abi.lib()
+
+
+def test_planner_invariants_over_random_problems():
+    """Seeded random shapes, dtypes, flag sets and budgets: every plan the
+    library returns is within its budget, covers the problem with bands of
+    whole 256-wide tiles, and reports sizes that agree with each other; every
+    refusal is one of the documented codes."""
+    import random
+
+    import torch
+    rng = random.Random(1234)
+    lib = L.lib()
+    flag_bits = [0, _abi.FLCE_FLAG_COMPACT_IGNORED, _abi.FLCE_FLAG_BF16_GRADS,
+                 _abi.FLCE_FLAG_SORT_VOCAB, _abi.FLCE_FLAG_FILTER_FULL_C,
+                 _abi.FLCE_FLAG_FILTER_FULL_E]
+    ok = 0
+    for _ in range(3000):
+        N = rng.choice([0, 1, rng.randint(1, 300), rng.randint(1, 20000), rng.randint(1, 300000)])
+        D = 8 * rng.randint(1, rng.choice([4, 64, 1024]))
+        V = rng.choice([1, rng.randint(1, 5000), rng.randint(1, 300000)])
+        dt = rng.choice([torch.bfloat16, torch.float32])
+        flags = 0
+        for b in flag_bits:
+            if rng.random() < 0.3:
+                flags |= b
+        eps = rng.choice([0.0, 2.0 ** -12])
+        budget = rng.choice([0, rng.randint(1, 128) * MiB, rng.randint(1, 4096) * 1024])
+        d = L.make_desc(N, D, V, dtype=dt, filter_eps=eps, flags=flags, ws_budget_bytes=budget)
+        info = _abi.FlcePlanInfo()
+        rc = lib.flce_plan(ctypes.byref(d), ctypes.byref(info))
+        if rc != _abi.FLCE_OK:
+            assert rc in (_abi.FLCE_E_WORKSPACE, _abi.FLCE_E_UNSUPPORTED), rc
+            assert lib.flce_workspace_bytes(ctypes.byref(d)) == 0
+            continue
+        ok += 1
+        es = 2 if dt == torch.bfloat16 else 4
+        sort = bool(flags & _abi.FLCE_FLAG_SORT_VOCAB) and eps > 0
+        assert info.ws_bytes == lib.flce_workspace_bytes(ctypes.byref(d))
+        assert info.ws_bytes <= (budget or 64 * MiB)
+        assert info.band_rows % 256 == 0 and info.band_vocab % 256 == 0
+        assert info.band_vocab <= (4096 if sort else 8192)
+        assert info.n_bands_rows * info.band_rows >= max(N, 1)
+        assert (info.n_bands_rows - 1) * info.band_rows < max(N, 1)
+        assert info.n_bands_vocab * info.band_vocab >= V > (info.n_bands_vocab - 1) * info.band_vocab
+        assert info.dz_bytes == info.band_rows * info.band_vocab * es
+        assert info.fwd_band_rows % 256 == 0 and info.fwd_band_rows >= 256
+        if sort:
+            assert 0 < info.vocab_order_offset and info.vocab_order_offset + 8 * V <= info.ws_bytes
+        else:
+            assert info.vocab_order_offset == -1
+    assert ok > 1000

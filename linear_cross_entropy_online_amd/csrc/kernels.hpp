@@ -564,7 +564,10 @@ struct DzArgs {
 
 // dZ tile t of a band: Z = W_v H_n^T recomputed, G = softmax(Z) - onehot(y),
 // dZ = g G (bf16 for bf16 inputs), plus the 64x64 filter flags.
-template <typename T>
+// FILTER false: no block decision is needed (a block would be dropped only
+// if all of it is zero, which changes no value), so the softmax goes out one
+// 32-row block at a time and no flags are written.
+template <typename T, bool FILTER = true>
 __device__ __forceinline__ void dz_tile(const DzArgs<T>& a, int t, char* lds) {
   const T* __restrict__ H = a.H;
   const T* __restrict__ W = a.W;
@@ -614,6 +617,60 @@ __device__ __forceinline__ void dz_tile(const DzArgs<T>& a, int t, char* lds) {
   }
   const int fr0 = (n0 - band.nb0 + wn * 128) >> 6;   // flag row of this wave's first 64 rows
   const int fc0 = (v0 - band.vb0 + wm * 128) >> 6;   // flag column of its first 64 vocab rows
+  // dZ = g (p - onehot).  bf16: into the LDS copy of the tile ([256 token
+  // rows][512 B], 16-byte chunk c of row r at chunk c ^ (r % 32), so the 32
+  // rows one instruction writes spread over all banks), stored to the band
+  // below in whole rows.  fp32: straight to the band.  Column block j of the
+  // wave (32 token rows), scale gg(i) for row block i.
+  auto store_block = [&](int j, const float (&pj)[4][16], float gA, float gB) {
+    const int r = wn * 128 + j * 32 + (lane & 31);   // tile row
+    T* row = dz + (int64_t)(n0 - band.nb0 + r) * band.ldz + (vw - band.vb0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float gg = i < 2 ? gA : gB;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = i * 32 + 8 * q + 4 * (lane >> 5);        // column within the wave's 128
+        if constexpr (sizeof(T) == 2) {
+          const int col = wm * 128 + c;                          // tile column
+          *reinterpret_cast<u32x2*>(lds + r * 512 + (((col >> 3) ^ (r & 31)) * 16) +
+                                    ((col >> 2) & 1) * 8) =
+              u32x2{pack_bf16x2(gg * pj[i][4 * q + 0], gg * pj[i][4 * q + 1]),
+                    pack_bf16x2(gg * pj[i][4 * q + 2], gg * pj[i][4 * q + 3])};
+        } else {
+          store4<T>(row + c, gg * pj[i][4 * q + 0], gg * pj[i][4 * q + 1],
+                    gg * pj[i][4 * q + 2], gg * pj[i][4 * q + 3]);
+        }
+      }
+    }
+  };
+  if constexpr (!FILTER) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float pj[4][16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pj[i][r] = fast_exp2(fmaf(acc[i][j][r], kLog2e, -ml[j]));
+      if (vw + 128 > V) {   // vocabulary rows past V (last tile)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (vw + acc_row(i, r, lane) >= V) pj[i][r] = 0.f;
+      }
+      const int rl = rel[j];
+      const bool hit = (unsigned)rl < 128u;
+      if (__any(hit)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (hit && rl == acc_row(i, r, lane)) pj[i][r] -= 1.f;
+      }
+      store_block(j, pj, g[j], g[j]);
+    }
+  } else {
   // One pair of 32-column blocks (64 token rows) at a time, so at most 128
   // softmax values sit in VGPRs while the accumulators stay where they are.
 #pragma unroll
@@ -679,33 +736,9 @@ __device__ __forceinline__ void dz_tile(const DzArgs<T>& a, int t, char* lds) {
         flagsT[fc * band.frows + fr] = kp ? 0 : 1;
       }
     }
-    // dZ = g (p - onehot).  bf16: into the LDS copy of the tile ([256 token
-    // rows][512 B], 16-byte chunk c of row r at chunk c ^ (r % 32), so the 32
-    // rows one instruction writes spread over all banks), stored to the band
-    // below in whole rows.  fp32: straight to the band.
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int r = wn * 128 + (2 * bj + jj) * 32 + (lane & 31);   // tile row
-      T* row = dz + (int64_t)(n0 - band.nb0 + r) * band.ldz + (vw - band.vb0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float gg = gk[i >> 1][jj];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = i * 32 + 8 * q + 4 * (lane >> 5);        // column within the wave's 128
-          if constexpr (sizeof(T) == 2) {
-            const int col = wm * 128 + c;                          // tile column
-            *reinterpret_cast<u32x2*>(lds + r * 512 + (((col >> 3) ^ (r & 31)) * 16) +
-                                      ((col >> 2) & 1) * 8) =
-                u32x2{pack_bf16x2(gg * p[jj][i][4 * q + 0], gg * p[jj][i][4 * q + 1]),
-                      pack_bf16x2(gg * p[jj][i][4 * q + 2], gg * p[jj][i][4 * q + 3])};
-          } else {
-            store4<T>(row + c, gg * p[jj][i][4 * q + 0], gg * p[jj][i][4 * q + 1],
-                      gg * p[jj][i][4 * q + 2], gg * p[jj][i][4 * q + 3]);
-          }
-        }
-      }
-    }
+    store_block(2 * bj, p[0], gk[0][0], gk[1][0]);
+    store_block(2 * bj + 1, p[1], gk[0][1], gk[1][1]);
+  }
   }
   if constexpr (sizeof(T) == 2) {
     // The tile's 128 KiB of bf16 dZ from LDS to the band: wave w stores rows
@@ -1088,7 +1121,7 @@ bwd_band_kernel(GradArgs<T> ga, DzArgs<T> da, int g_long, int g_grad, int h_firs
       lds[(COMPACT || SORT) && kBandLdsCompact > kLdsBytes ? kBandLdsCompact : kLdsBytes];
   const int t = xcd_remap_kinds(blockIdx.x, gridDim.x, g_long, g_grad);
   if (t >= g_grad) {
-    dz_tile<T>(da, t - g_grad, lds);
+    dz_tile<T, FILTER>(da, t - g_grad, lds);
     return;
   }
   const int T3 = ga.Td * ga.T3n;   // dH^T tiles

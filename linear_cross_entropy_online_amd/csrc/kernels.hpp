@@ -1056,53 +1056,110 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
   const bool scatter = (COMPACT && is_h) || (SORT && !is_h);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(
       scatter ? (is_h ? dH : dW) : out + (int64_t)row0 * D));
-  // Two row groups in flight: the loads of group j + 1 (and j + 2) are out
-  // while group j is added and stored.
-  auto offsets = [&](int j, uint32_t (&off)[4][4]) {
-    const int lr = lw + 32 * j;
-    const bool rok = row0 + lr < rvalid;
-    const int64_t orow = scatter ? (rok ? (int64_t)smap[lr] : 0) : lr;
+  if constexpr (std::is_same_v<T, float>) {
+    // Float inputs keep their accumulators in VGPRs, where staging through
+    // LDS spills: the epilogue goes straight from the accumulators, two row
+    // groups in flight (the loads of group j + 1 and j + 2 are out while
+    // group j is added and stored).
+    auto offsets = [&](int j, uint32_t (&off)[4][4]) {
+      const int lr = lw + 32 * j;
+      const bool rok = row0 + lr < rvalid;
+      const int64_t orow = scatter ? (rok ? (int64_t)smap[lr] : 0) : lr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int d = dw + 32 * i + 8 * q;
-        off[i][q] = rok && d < D ? (uint32_t)((orow * D + d) * 4) : kOob;
+        for (int q = 0; q < 4; ++q) {
+          const int d = dw + 32 * i + 8 * q;
+          off[i][q] = rok && d < D ? (uint32_t)((orow * D + d) * 4) : kOob;
+        }
+    };
+    auto load = [&](const uint32_t (&off)[4][4], f32x4 (&old)[4][4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          old[i][q] = beta ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           rs, off[i][q], 0, 0))
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto store = [&](int j, const uint32_t (&off)[4][4], const f32x4 (&old)[4][4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = f32x4{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                acc[i][j][4 * q + 3]} + old[i][q];
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off[i][q], 0,
+                                                 0);
+        }
+    };
+    uint32_t offA[4][4], offB[4][4];
+    f32x4 oldA[4][4], oldB[4][4];
+    offsets(0, offA);
+    load(offA, oldA);
+    offsets(1, offB);
+    load(offB, oldB);
+    store(0, offA, oldA);
+    offsets(2, offA);
+    load(offA, oldA);
+    store(1, offB, oldB);
+    offsets(3, offB);
+    load(offB, oldB);
+    store(2, offA, oldA);
+    store(3, offB, oldB);
+    return;
+  }
+  // bf16 inputs: the tile's rows go through LDS, one half (128 rows) at a
+  // time: the waves that hold the half write their accumulators row-major (16-byte chunk c
+  // of row r at chunk c ^ (r % 32), which spreads a column of chunks over
+  // all banks), then every wave adds and stores 32 whole rows, so each load
+  // and store instruction covers one 1 KiB row of the tile instead of 32
+  // bytes of 64 rows.  Both contraction cores end with a barrier, so the
+  // staging slots are free here.
+  const int dcol = td * kTile + lane * 4;   // this lane's 4 columns
+  const bool dok = dcol < D;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (wn == half) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 32 * j + (lane & 31);
+            const int c = wm * 32 + 8 * i + 2 * q + (lane >> 5);
+            *reinterpret_cast<f32x4*>(lds + r * 1024 + ((c ^ (r & 31)) * 16)) =
+                f32x4{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                      acc[i][j][4 * q + 3]};
+          }
+    }
+    __syncthreads();
+    constexpr int R = 16;   // rows in flight per wave
+#pragma unroll
+    for (int b = 0; b < 32 / R; ++b) {
+      uint32_t ro[R];
+      f32x4 old[R];
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int trow = half * 128 + wave * 32 + b * R + k;    // row within the tile
+        const bool rok = row0 + trow < rvalid;
+        const int64_t orow = scatter ? (rok ? (int64_t)smap[trow] : 0) : trow;
+        ro[k] = rok && dok ? (uint32_t)((orow * D + dcol) * 4) : kOob;
+        old[k] = beta ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rs, ro[k], 0, 0))
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
       }
-  };
-  auto load = [&](const uint32_t (&off)[4][4], f32x4 (&old)[4][4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        old[i][q] = beta ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                         rs, off[i][q], 0, 0))
-                         : f32x4{0.f, 0.f, 0.f, 0.f};
-  };
-  auto store = [&](int j, const uint32_t (&off)[4][4], const f32x4 (&old)[4][4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = f32x4{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                              acc[i][j][4 * q + 3]} + old[i][q];
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off[i][q], 0, 0);
+      for (int k = 0; k < R; ++k) {
+        const int rl = wave * 32 + b * R + k;                    // row within the half
+        const f32x4 v =
+            *reinterpret_cast<const f32x4*>(lds + rl * 1024 + ((lane ^ (rl & 31)) * 16)) + old[k];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, ro[k], 0, 0);
       }
-  };
-  uint32_t offA[4][4], offB[4][4];
-  f32x4 oldA[4][4], oldB[4][4];
-  offsets(0, offA);
-  load(offA, oldA);
-  offsets(1, offB);
-  load(offB, oldB);
-  store(0, offA, oldA);
-  offsets(2, offA);
-  load(offA, oldA);
-  store(1, offB, oldB);
-  offsets(3, offB);
-  load(offB, oldB);
-  store(2, offA, oldA);
-  store(3, offB, oldB);
+    }
+    __syncthreads();
+  }
 }
 
 // One launch of the backward pipeline: the gradient tiles of band k - 1

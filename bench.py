@@ -415,6 +415,26 @@ def main():
                     "traffic": traffic, "flops_per_launch": per_launch,
                     "avg_launch_ms": kernels[dom]["avg_ms"]}
 
+    # the forward contraction on its own: 2 N D V flop per launch
+    forward = None
+    if "fwd_lse" in kernels:
+        f_ms = kernels["fwd_lse"]["ms_per_step"]
+        f_tf = flops_per_step["fwd_lse"] / (f_ms * 1e-3) / 1e12
+        forward = {"ms": round(f_ms, 4), "tflops": round(f_tf, 1), "frac": round(f_tf / peak, 4)}
+
+    # the gradient filter: K blocks of 64 the filtered products ran, of those
+    # that exist (last step); executed flop scales the filtered products
+    filt = None
+    if args.filter_eps > 0:
+        act, tot = L.flce_filter_stats(ws)
+        kept = act / tot if tot else 1.0
+        filtered = 4.0 * n_eff * D * V            # dH and dW products
+        executed = counted - filtered * (1.0 - kept)
+        filt = {"kblocks_active": act, "kblocks_total": tot, "skip_fraction": round(1 - kept, 4),
+                "tflop_counted_8ndv": round(counted / 1e12, 3),
+                "tflop_executed": round(executed / 1e12, 3),
+                "executed_tflops": round(executed / (ms * 1e-3) / 1e12, 1)}
+
     cpu = None
     if args.cpu_rows > 0:
         print(f"bench: cpu_baseline oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
@@ -440,7 +460,8 @@ def main():
                                         / 2**20, 1),
         "plan": {"band_rows": NS, "band_vocab": VS, "bands": n_bands,
                  "fwd_band_rows": plan["fwd_band_rows"], "fwd_workgroups": plan["fwd_workgroups"]},
-        "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
+        "kernels": kernels, "forward": forward, "filter": filt, "roofline": roofline,
+        "cpu_baseline": cpu,
         "grads_in_forward_scale_ms": None if scale_ms is None else round(scale_ms, 4),
     }
     print(json.dumps(line), flush=True)

@@ -29,7 +29,7 @@
  *     16-byte aligned.
  *   - Work is enqueued on `stream` (0 = the null stream) and runs
  *     asynchronously; no entry point synchronises except
- *     flce_device_status().  Outputs are overwritten, never accumulated.
+ *     flce_device_status() and flce_filter_stats().  Outputs are overwritten, never accumulated.
  *   - Argument errors are reported synchronously by the return code, before
  *     anything is enqueued; outputs are then untouched.
  *   - A target outside [0, V) that is not ignore_index is detected on the
@@ -226,6 +226,20 @@ int flce_scale_gradients(const flce_desc* d, const float* dloss, void* dH, void*
 /* Synchronises `stream`, then reads the status word of `ws` into *out
  * (bit 0: a target outside [0, V) that is not ignore_index). */
 int flce_device_status(const void* ws, hipStream_t stream, int32_t* out);
+
+/* Work the gradient filter left out (CCE Sec. 4.3, "Gradient filtering",
+ * and Algorithm 4: a K step of a gradient contraction is skipped when every
+ * block of softmax - onehot it covers is below filter_eps).  Synchronises
+ * `stream`, then reads from `ws` the 64-wide K blocks of the filtered
+ * gradient contractions of the last flce_backward or flce_fused_fwd_bwd call
+ * on this workspace (a later flce_forward on it clears them): *active =
+ * blocks that ran, *total = blocks that exist,
+ * summed over the tiles (each block of a tile is 256 x 256 x 64
+ * multiply-adds).  Only the products the filter acts on are counted (both,
+ * or the one FLCE_FLAG_FILTER_FULL_C / _FULL_E leaves filtered); with the
+ * filter off both are 0.  The skip fraction is 1 - active / total.  Returns
+ * FLCE_E_NULL for a NULL argument, FLCE_E_DEVICE if a HIP call fails. */
+int flce_filter_stats(const void* ws, hipStream_t stream, int64_t* active, int64_t* total);
 
 /* Static description of a return code. */
 const char* flce_strerror(int code);

@@ -12,6 +12,7 @@ Functions with the C ABI's names take torch tensors:
     flce_backward(H, W, y, lse, dloss=None, ...)   -> (dH, dW)
     flce_fused_fwd_bwd(H, W, y, ...)               -> (loss, loss_rows, lse, dH, dW)
     flce_device_status(ws)                         -> int
+    flce_filter_stats(ws)                          -> (active, total) K blocks
 and ``linear_cross_entropy(H, W, y, ...)`` is an autograd function over the
 forward / backward pair.
 """
@@ -30,8 +31,8 @@ from ._abi import (FLCE_BF16, FLCE_F32, FLCE_FLAG_BF16_GRADS, FLCE_FLAG_COMPACT_
                    FLCE_K_LSE_COMBINE, FLCE_MEAN, FLCE_NONE, FLCE_SUM, FlceError, lib)
 
 __all__ = ["flce_workspace_bytes", "flce_plan", "flce_forward", "flce_backward",
-           "flce_fused_fwd_bwd", "flce_scale_gradients", "flce_device_status", "flce_profile_reset",
-           "flce_profile_read", "linear_cross_entropy", "Workspace", "FlceError", "lib",
+           "flce_fused_fwd_bwd", "flce_scale_gradients", "flce_filter_stats", "flce_device_status",
+           "flce_profile_reset", "flce_profile_read", "linear_cross_entropy", "Workspace", "FlceError", "lib",
            "FLCE_FLAG_PROFILE", "FLCE_FLAG_COMPACT_IGNORED", "FLCE_FLAG_BF16_GRADS",
            "FLCE_FLAG_FILTER_FULL_C", "FLCE_FLAG_FILTER_FULL_E", "FLCE_FLAG_SORT_VOCAB",
            "KERNEL_CLASSES"]
@@ -214,6 +215,16 @@ def flce_scale_gradients(dH, dW, dloss, reduction="mean", dtype=torch.bfloat16):
     _abi.check(lib().flce_scale_gradients(ctypes.byref(d), _ptr(dloss), _ptr(dH), _ptr(dW),
                                           _stream(dW.device)))
     return dH, dW
+
+
+def flce_filter_stats(ws: Workspace, device=None) -> tuple[int, int]:
+    """(active, total) 64-wide K blocks of the filtered gradient contractions
+    of the last backward on ``ws`` (synchronises the stream)."""
+    active, total = ctypes.c_int64(0), ctypes.c_int64(0)
+    dev = ws.buf.device if device is None else device
+    _abi.check(lib().flce_filter_stats(ws.ptr(), _stream(dev), ctypes.byref(active),
+                                       ctypes.byref(total)))
+    return int(active.value), int(total.value)
 
 
 def flce_device_status(ws: Workspace, device=None) -> int:

@@ -22,7 +22,8 @@ FLCE_FLAG_SORT_VOCAB = 32
 
 # Every function include/flce.h declares (checked against the header by a CPU test).
 EXPORTS = ["flce_workspace_bytes", "flce_plan", "flce_forward", "flce_backward",
-           "flce_fused_fwd_bwd", "flce_scale_gradients", "flce_device_status", "flce_strerror",
+           "flce_fused_fwd_bwd", "flce_scale_gradients", "flce_filter_stats", "flce_device_status",
+           "flce_strerror",
            "flce_profile_reset", "flce_profile_read", "flce_version"]
 
 
@@ -74,6 +75,9 @@ def lib():
     L.flce_fused_fwd_bwd.restype = i32
     L.flce_scale_gradients.argtypes = [pd, vp, vp, vp, vp]
     L.flce_scale_gradients.restype = i32
+    L.flce_filter_stats.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int64),
+                                    ctypes.POINTER(ctypes.c_int64)]
+    L.flce_filter_stats.restype = i32
     L.flce_device_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
     L.flce_device_status.restype = i32
     L.flce_strerror.argtypes = [i32]

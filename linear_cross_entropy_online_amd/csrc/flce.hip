@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -449,6 +450,12 @@ void band_kernel(bool filt, bool compact, bool sort, dim3 grid, hipStream_t s,
                                                                          h_first);
 }
 
+// The gradient filter's K-block counters in the workspace header.
+unsigned long long* kblk_counters(const Ws& w) {
+  return reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(w.hdr) +
+                                               offsetof(flce::Header, kblk));
+}
+
 // Bands k = 0 .. nb-1 (token-row band outer, vocabulary band inner).  Launch
 // k runs the gradient tiles of band k - 1 and the dZ tiles of band k, with
 // band k's dZ in buffer k % 2: the first launch only makes dZ, the last only
@@ -504,7 +511,7 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
                              Td, bv > 0 ? 1 : 0, bn > 0 ? 1 : 0, skip_h, skip_w, w.rowmap, w.hdr,
                              p.bf16g ? static_cast<uint16_t*>(dH) : nullptr,
                              p.bf16g ? static_cast<uint16_t*>(dW) : nullptr, w.stage, h_mode,
-                             w.vperm};
+                             w.vperm, filt ? kblk_counters(w) : nullptr};
   };
   if (p.bf16g) {
     if constexpr (sizeof(T) == 2) {
@@ -693,6 +700,18 @@ int flce_scale_gradients(const flce_desc* d, const float* dloss, void* dH, void*
   };
   if (p.N > 0) FLCE_TRY(scale(dH, p.N * p.D));
   return scale(dW, p.V * p.D);
+}
+
+int flce_filter_stats(const void* ws, hipStream_t stream, int64_t* active, int64_t* total) {
+  if (!ws || !active || !total) return FLCE_E_NULL;
+  if (hipStreamSynchronize(stream) != hipSuccess) return FLCE_E_DEVICE;
+  unsigned long long v[2] = {0, 0};
+  if (hipMemcpy(v, static_cast<const char*>(ws) + offsetof(flce::Header, kblk), sizeof(v),
+                hipMemcpyDeviceToHost) != hipSuccess)
+    return FLCE_E_DEVICE;
+  *active = int64_t(v[0]);
+  *total = int64_t(v[1]);
+  return FLCE_OK;
 }
 
 int flce_device_status(const void* ws, hipStream_t stream, int32_t* out) {

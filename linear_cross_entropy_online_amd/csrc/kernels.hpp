@@ -35,8 +35,12 @@ struct Header {           // first 256 bytes of the workspace
   int count;              // non-ignored rows
   float gscale;           // g for mean / sum: dloss / max(count, 1) or dloss
   int nvalid;             // with row compaction: rows whose target is not ignore_index
-  float pad[60];
+  // gradient filter: 64-wide K blocks of the filtered gradient contractions
+  // that ran / that exist, summed over the tiles of the last backward
+  unsigned long long kblk[2];
+  float pad[56];
 };
+static_assert(sizeof(Header) == 256, "the header is the first 256 bytes of the workspace");
 
 // The LDS row table of a compacted dW^T contraction holds NS / 2 entries per
 // parity, i.e. 32 per 64-row filter block of the band.
@@ -348,6 +352,7 @@ finalize_kernel(const double* __restrict__ blk_sum, const int* __restrict__ blk_
     const float up = dloss ? dloss[0] : 1.f;
     hdr->count = c;
     hdr->gscale = reduction == 0 ? up / (float)cl : up;
+    hdr->kblk[0] = hdr->kblk[1] = 0ull;
   }
 }
 
@@ -373,6 +378,7 @@ bwd_prep_kernel(const int64_t* __restrict__ y, int N, int V, int64_t ignore, int
     hdr->status = s > 0.0 ? 1 : 0;
     hdr->count = c;
     hdr->gscale = reduction == 0 ? up / (float)cl : up;
+    hdr->kblk[0] = hdr->kblk[1] = 0ull;
   }
 }
 
@@ -515,6 +521,7 @@ __global__ void clear_status_kernel(Header* __restrict__ hdr, float* __restrict_
   if (threadIdx.x == 0) {
     hdr->status = 0;
     hdr->count = 0;
+    hdr->kblk[0] = hdr->kblk[1] = 0ull;
     if (loss) *loss = 0.f;
   }
 }
@@ -770,22 +777,27 @@ struct SkipRowsOfFlags {
   int step_stride;         // bytes between consecutive 64-blocks
   int all = 0;             // every step active (the product is not filtered)
   uint64_t lo = 0, hi = 0; // bit b of (hi:lo): 64-block b is active
+  unsigned long long* ctr = nullptr;   // optional: += active and total 64-blocks
+  // Lane L of every wave reads the flags of 64-blocks L and 64 + L (indices
+  // clamped to the last block, so every read is inside the tile's flags) and
+  // two ballots give the masks: one round trip for the whole K range.
   __device__ __forceinline__ void prepare(int nsteps) {
-    const int nb = (nsteps + (1 << kShift) - 1) >> kShift;
-    uint64_t m0 = 0, m1 = 0;
-    for (int b = 0; b < nb && b < 64; ++b) {
-      const uint32_t f = *reinterpret_cast<const uint32_t*>(base + b * step_stride);
-      m0 |= (uint64_t)(f != 0x01010101u) << b;
-    }
-    for (int b = 64; b < nb && b < kMaxBlocks; ++b) {
-      const uint32_t f = *reinterpret_cast<const uint32_t*>(base + b * step_stride);
-      m1 |= (uint64_t)(f != 0x01010101u) << (b - 64);
-    }
+    const int nb = min((nsteps + (1 << kShift) - 1) >> kShift, kMaxBlocks);
+    const int lane = threadIdx.x & 63, last = nb > 0 ? nb - 1 : 0;
+    const uint32_t f0 = *reinterpret_cast<const uint32_t*>(base + min(lane, last) * step_stride);
+    const uint32_t f1 =
+        *reinterpret_cast<const uint32_t*>(base + min(lane + 64, last) * step_stride);
+    const uint64_t m0 = __ballot(lane < nb && f0 != 0x01010101u);
+    const uint64_t m1 = __ballot(lane + 64 < nb && f1 != 0x01010101u);
     // (a select, not a branch: a branch here makes the compiler treat the
     // tile's operand descriptors as divergent)
     const uint64_t every = all ? ~0ull : 0ull;
     lo = m0 | every;
     hi = m1 | every;
+    if (ctr != nullptr && !all && threadIdx.x == 0) {
+      atomicAdd(ctr, (unsigned long long)(__popcll(m0) + __popcll(m1)));
+      atomicAdd(ctr + 1, (unsigned long long)nb);
+    }
   }
   __device__ __forceinline__ bool operator()(int s) const {
     const int b = s >> kShift;
@@ -808,6 +820,7 @@ struct SkipRowsOfFlags {
     return ns < nsteps ? ns : nsteps;
   }
 };
+
 
 // dH[band rows] (+)= dZ W[band vocab] and dW[band vocab] (+)= dZ^T H[band rows]
 // in one launch.  Both products are computed transposed, C[d][row], so that
@@ -841,6 +854,7 @@ struct GradArgs {
   float* stage;
   int h_mode;
   const int* vperm;        // SORT: band vocabulary position p is row vperm[p] of W and dW
+  unsigned long long* kblk;   // FILTER: Header::kblk (active, total K blocks), else null
 };
 
 // Epilogue of a gradient tile with bf16 in or out: out[r][d] = acc + src[r][d]
@@ -967,12 +981,12 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
       gather_table(table, a.vperm + band.vb0, band.vs_cur, half);
       const Operand A{reinterpret_cast<const char*>(W), D, D, band.vs_cur,
                       reinterpret_cast<const int*>(table), half};
-      const SkipRowsOfFlags<step_k<T>()> act{flagsT + tr * 4, band.frows, !a.skip_h};
+      const SkipRowsOfFlags<step_k<T>()> act{flagsT + tr * 4, band.frows, !a.skip_h, 0, 0, a.kblk};
       tile_contract<T, true, false, SkipRowsOfFlags<step_k<T>()>, true>(
           A, B, td * kTile, tr * kTile, band.vs_cur, act, acc, lds);
     } else if constexpr (FILTER) {
       const Operand A{reinterpret_cast<const char*>(W + (int64_t)band.vb0 * D), D, D, band.vs_cur};
-      const SkipRowsOfFlags<step_k<T>()> act{flagsT + tr * 4, band.frows, !a.skip_h};
+      const SkipRowsOfFlags<step_k<T>()> act{flagsT + tr * 4, band.frows, !a.skip_h, 0, 0, a.kblk};
       tile_contract<T, true, false>(A, B, td * kTile, tr * kTile, band.vs_cur, act, acc, lds);
     } else {
       const Operand A{reinterpret_cast<const char*>(W + (int64_t)band.vb0 * D), D, D, band.vs_cur};
@@ -993,7 +1007,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
                       reinterpret_cast<const int*>(table), half};
       const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2n * kTile, K};
       if constexpr (FILTER) {
-        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols, !a.skip_w};
+        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols, !a.skip_w, 0, 0, a.kblk};
         tile_contract<T, true, true, SkipRowsOfFlags<step_k<T>()>, true>(A, B, td * kTile,
                                                                         tr * kTile, K, act, acc,
                                                                         lds);
@@ -1005,7 +1019,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
       const Operand A{reinterpret_cast<const char*>(H + (int64_t)band.nb0 * D), D, D, band.ns_cur};
       const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2n * kTile, band.ns_cur};
       if constexpr (FILTER) {
-        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols, !a.skip_w};
+        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols, !a.skip_w, 0, 0, a.kblk};
         tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, act, acc, lds);
       } else {
         tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, AllActive{}, acc,

@@ -273,6 +273,37 @@ def filter_block_stats(H, W, y, lse, eps: float, block=(64, 64), rows=None,
     return dropped / max(total, 1)
 
 
+def filter_block_max(H, W, y, ignore_index: int = IGNORE_INDEX_DEFAULT, block=(64, 64),
+                     order=None, row_chunk: int = 256) -> np.ndarray:
+    """max |softmax - onehot| over the non-ignored rows of every (row block,
+    vocabulary block) of G (CCE Alg. 4's quantity: a block is dropped iff
+    this is below eps), shape [ceil(N / rows), ceil(V / vocab)]; 0 for a block
+    with no non-ignored row.  Vocabulary blocks run over ``order`` (the
+    natural order if None).  Blocks are anchored at row 0 and position 0."""
+    H = _f64(H)
+    W = _f64(W)
+    y = _i64(y)
+    N = H.shape[0]
+    V = W.shape[0]
+    nb, vb = block
+    valid = valid_rows(y, V, ignore_index)
+    order = np.arange(V) if order is None else np.asarray(order)
+    out = np.zeros(((N + nb - 1) // nb, (V + vb - 1) // vb))
+    row_chunk = max(nb, (row_chunk // nb) * nb)
+    for r0 in range(0, N, row_chunk):
+        r1 = min(N, r0 + row_chunk)
+        Z = H[r0:r1] @ W.T
+        G = np.exp(Z - _lse(Z)[:, None])
+        vr = valid[r0:r1]
+        G[np.nonzero(vr)[0], y[r0:r1][vr]] -= 1.0
+        G[~vr] = 0.0
+        A = np.abs(G[:, order])
+        for a in range(0, r1 - r0, nb):
+            for b in range(0, V, vb):
+                out[(r0 + a) // nb, b // vb] = A[a:a + nb, b:b + vb].max()
+    return out
+
+
 def filtered_block_samples(H, W, y, lse, g, eps: float, row_blocks, vocab_blocks,
                            block=(64, 64), ignore_index: int = IGNORE_INDEX_DEFAULT):
     """dH rows of whole row blocks and dW rows of whole vocabulary blocks under

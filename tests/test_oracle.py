@@ -336,6 +336,34 @@ def test_sorted_vocabulary_filter_brute_force():
     assert np.array_equal(a["dH"], b["dH"]) and np.array_equal(a["dW"], b["dW"])
 
 
+@pytest.mark.parametrize("block,sort", [((4, 2), False), ((2, 4), False), ((4, 4), True)])
+def test_filter_block_max_brute_force(block, sort):
+    """Per-block max |softmax - onehot| by loops over the definition (ignored
+    rows left out, an all-ignored block is 0); unequal block shapes catch a
+    transposed index, a ragged edge (13 rows, 19 entries) the partial blocks."""
+    H, W, y = _case(13, 5, 19, seed=18, ignore_frac=0.3, sigma_w=3.0)
+    y[0:4] = -100                       # one all-ignored 4-row block
+    N, D = H.shape
+    V = W.shape[0]
+    nb, vb = block
+    order = list(O.vocab_order(H, W, y, row_chunk=4)) if sort else list(range(V))
+    want = np.zeros(((N + nb - 1) // nb, (V + vb - 1) // vb))
+    for n in range(N):
+        if int(y[n]) == -100:
+            continue
+        z = [sum(H[n, k] * W[v, k] for k in range(D)) for v in range(V)]
+        m = max(z)
+        lse = m + math.log(sum(math.exp(t - m) for t in z))
+        for p, v in enumerate(order):
+            gv = abs(math.exp(z[v] - lse) - (1.0 if v == y[n] else 0.0))
+            want[n // nb, p // vb] = max(want[n // nb, p // vb], gv)
+    got = O.filter_block_max(H, W, y, block=block, order=order if sort else None, row_chunk=4)
+    assert got.shape == want.shape
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
+    if nb == 4:
+        assert np.all(got[0] == 0.0)
+
+
 def test_sorted_vocabulary_groups_the_likely_tokens():
     """Entries with a high average logit end up in the leading blocks: when a
     few scattered vocabulary entries carry the whole softmax for every row,

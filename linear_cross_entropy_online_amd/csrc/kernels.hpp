@@ -857,85 +857,91 @@ struct GradArgs {
   unsigned long long* kblk;   // FILTER: Header::kblk (active, total K blocks), else null
 };
 
-// Epilogue of a gradient tile with bf16 in or out: out[r][d] = acc + src[r][d]
+// Epilogue of a gradient tile for bf16 inputs: out[r][d] = acc + src[r][d]
 // (src optional) for the tile rows r < rvalid - row0 and d < D.  src rows are
-// the tile's rows (SRC_MAPPED: map[r] like the out rows); out rows are the
-// same or, with `map`, map[r].  Same two-row-groups-in-flight order as the
-// float epilogue; bf16 values are widened exactly and rounded to nearest even
-// once.
+// the tile's rows (SRC_MAPPED: map[r], like the out rows); out rows are the
+// same or, with `map`, map[r].  The rows go through LDS half a tile (128
+// rows) at a time: the waves holding the half write their accumulators
+// row-major (16-byte chunk c of row r at chunk c ^ (r % 32), which spreads a
+// column of chunks over all banks), then every wave adds and stores 32 whole
+// rows, so one load or store instruction covers a whole row of the tile (1 KiB
+// of floats, 512 B of bf16) instead of 16 or 32 bytes of 64 rows.  bf16
+// values are widened exactly and rounded to nearest even once.  Both
+// contraction cores end with a barrier, so the staging slots are free here.
 template <bool SRC_BF16, bool DST_BF16, bool SRC_MAPPED = false>
-__device__ __forceinline__ void grad_epilogue_cvt(const f32x16 (&acc)[4][4], bool src_on,
-                                                  __amdgpu_buffer_rsrc_t rsS,
-                                                  __amdgpu_buffer_rsrc_t rsD, const int* map,
-                                                  int row0, int rvalid, int D, int dw, int lw) {
+__device__ __forceinline__ void grad_epilogue_rows(const f32x16 (&acc)[4][4], bool src_on,
+                                                   __amdgpu_buffer_rsrc_t rsS,
+                                                   __amdgpu_buffer_rsrc_t rsD, const int* map,
+                                                   int row0, int rvalid, int D, int td,
+                                                   char* lds) {
   constexpr int SES = SRC_BF16 ? 2 : 4, DES = DST_BF16 ? 2 : 4;
-  auto offsets = [&](int j, uint32_t (&os)[4][4], uint32_t (&od)[4][4]) {
-    const int lr = lw + 32 * j;
-    const bool rok = row0 + lr < rvalid;
-    const int64_t orow = map ? (rok ? (int64_t)map[lr] : 0) : lr;
+  constexpr int R = 16;   // rows in flight per wave
+  using Old = std::conditional_t<SRC_BF16, u32x2, f32x4>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+  const int wm = wave >> 1, wn = wave & 1;
+  const int dcol = td * kTile + lane * 4;   // this lane's 4 columns
+  const bool dok = dcol < D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int half = 0; half < 2; ++half) {
+    if (wn == half) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int d = dw + 32 * i + 8 * q;
-        const bool ok = rok && d < D;
-        os[i][q] = ok ? (uint32_t)(((SRC_MAPPED ? orow : (int64_t)lr) * D + d) * SES) : kOob;
-        od[i][q] = ok ? (uint32_t)((orow * D + d) * DES) : kOob;
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 32 * j + (lane & 31);
+            const int c = wm * 32 + 8 * i + 2 * q + (lane >> 5);
+            *reinterpret_cast<f32x4*>(lds + r * 1024 + ((c ^ (r & 31)) * 16)) =
+                f32x4{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                      acc[i][j][4 * q + 3]};
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < 32 / R; ++b) {
+      uint32_t od[R];
+      Old old[R];
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int trow = half * 128 + wave * 32 + b * R + k;   // row within the tile
+        const bool rok = row0 + trow < rvalid, ok = rok && dok;
+        const int64_t orow = map ? (rok ? (int64_t)map[trow] : 0) : trow;   // uniform per wave
+        const uint32_t os = ok ? (uint32_t)(((SRC_MAPPED ? orow : (int64_t)trow) * D + dcol) * SES)
+                               : kOob;
+        od[k] = ok ? (uint32_t)((orow * D + dcol) * DES) : kOob;
+        if constexpr (SRC_BF16)
+          old[k] = src_on ? __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                          rsS, os, 0, 0))
+                          : u32x2{0u, 0u};
+        else
+          old[k] = src_on ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rsS, os, 0, 0))
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
       }
-  };
-  auto load = [&](const uint32_t (&os)[4][4], u32x4 (&old)[4][4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (SRC_BF16) {
-          const u32x2 v = src_on ? __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                                 rsS, os[i][q], 0, 0))
-                                 : u32x2{0u, 0u};
-          old[i][q] = u32x4{v[0], v[1], 0u, 0u};
-        } else {
-          old[i][q] = src_on ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                             rsS, os[i][q], 0, 0))
-                             : u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-  };
-  auto store = [&](int j, const uint32_t (&od)[4][4], const u32x4 (&old)[4][4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int k = 0; k < R; ++k) {
+        const int rl = wave * 32 + b * R + k;                     // row within the half
         f32x4 o;
         if constexpr (SRC_BF16)   // element d in the low half of a dword
-          o = f32x4{__builtin_bit_cast(float, old[i][q][0] << 16),
-                    __builtin_bit_cast(float, old[i][q][0] & 0xffff0000u),
-                    __builtin_bit_cast(float, old[i][q][1] << 16),
-                    __builtin_bit_cast(float, old[i][q][1] & 0xffff0000u)};
+          o = f32x4{__builtin_bit_cast(float, old[k][0] << 16),
+                    __builtin_bit_cast(float, old[k][0] & 0xffff0000u),
+                    __builtin_bit_cast(float, old[k][1] << 16),
+                    __builtin_bit_cast(float, old[k][1] & 0xffff0000u)};
         else
-          o = __builtin_bit_cast(f32x4, old[i][q]);
-        const f32x4 v = f32x4{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                              acc[i][j][4 * q + 3]} + o;
+          o = old[k];
+        const f32x4 v =
+            *reinterpret_cast<const f32x4*>(lds + rl * 1024 + ((lane ^ (rl & 31)) * 16)) + o;
         if constexpr (DST_BF16)
           __builtin_amdgcn_raw_buffer_store_b64(
-              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rsD, od[i][q], 0, 0);
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rsD, od[k], 0, 0);
         else
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsD, od[i][q], 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsD, od[k], 0, 0);
       }
-  };
-  uint32_t sA[4][4], dA[4][4], sB[4][4], dB[4][4];
-  u32x4 oldA[4][4], oldB[4][4];
-  offsets(0, sA, dA);
-  load(sA, oldA);
-  offsets(1, sB, dB);
-  load(sB, oldB);
-  store(0, dA, oldA);
-  offsets(2, sA, dA);
-  load(sA, oldA);
-  store(1, dB, oldB);
-  offsets(3, sB, dB);
-  load(sB, oldB);
-  store(2, dA, oldA);
-  store(3, dB, oldB);
+    }
+    __syncthreads();
+  }
 }
 
 // Gradient tile `local` of one of the band's two contractions (is_h: dH^T).
@@ -1040,24 +1046,26 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
       const int hm = a.h_mode;
       const auto rsS = make_rsrc(reinterpret_cast<const char*>(a.stage + (int64_t)row0 * D));
       if (hm <= 1) {
-        grad_epilogue_cvt<false, false>(acc, hm == 1, rsS, rsS, nullptr, row0, rvalid, D, dw, lw);
+        grad_epilogue_rows<false, false>(acc, hm == 1, rsS, rsS, nullptr, row0, rvalid, D, td,
+                                         lds);
       } else {
         // scattered rows: offsets from the start of dH (N D 4 < 2^31 with compaction)
         const auto rsD = make_rsrc(reinterpret_cast<const char*>(
             COMPACT ? a.dHb : a.dHb + ((int64_t)band.nb0 + row0) * D));
-        grad_epilogue_cvt<false, true>(acc, hm == 2, rsS, rsD,
-                                       COMPACT ? a.rowmap + band.nb0 + row0 : nullptr, row0,
-                                       rvalid, D, dw, lw);
+        grad_epilogue_rows<false, true>(acc, hm == 2, rsS, rsD,
+                                        COMPACT ? a.rowmap + band.nb0 + row0 : nullptr, row0,
+                                        rvalid, D, td, lds);
       }
     } else {
       if constexpr (SORT) {   // rows scattered: offsets from the start of dW (V D 4 < 2^31)
         const auto rs = make_rsrc(reinterpret_cast<const char*>(a.dWb));
-        grad_epilogue_cvt<true, true, true>(acc, beta_w != 0, rs, rs, a.vperm + band.vb0 + row0,
-                                            row0, rvalid, D, dw, lw);
+        grad_epilogue_rows<true, true, true>(acc, beta_w != 0, rs, rs, a.vperm + band.vb0 + row0,
+                                             row0, rvalid, D, td, lds);
       } else {
         const auto rs = make_rsrc(
             reinterpret_cast<const char*>(a.dWb + ((int64_t)band.vb0 + row0) * D));
-        grad_epilogue_cvt<true, true>(acc, beta_w != 0, rs, rs, nullptr, row0, rvalid, D, dw, lw);
+        grad_epilogue_rows<true, true>(acc, beta_w != 0, rs, rs, nullptr, row0, rvalid, D, td,
+                                       lds);
       }
     }
     return;
@@ -1123,57 +1131,8 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
     store(3, offB, oldB);
     return;
   }
-  // bf16 inputs: the tile's rows go through LDS, one half (128 rows) at a
-  // time: the waves that hold the half write their accumulators row-major (16-byte chunk c
-  // of row r at chunk c ^ (r % 32), which spreads a column of chunks over
-  // all banks), then every wave adds and stores 32 whole rows, so each load
-  // and store instruction covers one 1 KiB row of the tile instead of 32
-  // bytes of 64 rows.  Both contraction cores end with a barrier, so the
-  // staging slots are free here.
-  const int dcol = td * kTile + lane * 4;   // this lane's 4 columns
-  const bool dok = dcol < D;
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if (wn == half) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 32 * j + (lane & 31);
-            const int c = wm * 32 + 8 * i + 2 * q + (lane >> 5);
-            *reinterpret_cast<f32x4*>(lds + r * 1024 + ((c ^ (r & 31)) * 16)) =
-                f32x4{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                      acc[i][j][4 * q + 3]};
-          }
-    }
-    __syncthreads();
-    constexpr int R = 16;   // rows in flight per wave
-#pragma unroll
-    for (int b = 0; b < 32 / R; ++b) {
-      uint32_t ro[R];
-      f32x4 old[R];
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const int trow = half * 128 + wave * 32 + b * R + k;    // row within the tile
-        const bool rok = row0 + trow < rvalid;
-        const int64_t orow = scatter ? (rok ? (int64_t)smap[trow] : 0) : trow;
-        ro[k] = rok && dok ? (uint32_t)((orow * D + dcol) * 4) : kOob;
-        old[k] = beta ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      rs, ro[k], 0, 0))
-                      : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const int rl = wave * 32 + b * R + k;                    // row within the half
-        const f32x4 v =
-            *reinterpret_cast<const f32x4*>(lds + rl * 1024 + ((lane ^ (rl & 31)) * 16)) + old[k];
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, ro[k], 0, 0);
-      }
-    }
-    __syncthreads();
-  }
+  // bf16 inputs: whole rows through LDS (old values at the out rows)
+  grad_epilogue_rows<false, false, true>(acc, beta != 0, rs, rs, smap, row0, rvalid, D, td, lds);
 }
 
 // One launch of the backward pipeline: the gradient tiles of band k - 1

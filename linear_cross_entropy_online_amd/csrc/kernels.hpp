@@ -865,9 +865,13 @@ struct GradArgs {
 // row-major (16-byte chunk c of row r at chunk c ^ (r % 32), which spreads a
 // column of chunks over all banks), then every wave adds and stores 32 whole
 // rows, so one load or store instruction covers a whole row of the tile (1 KiB
-// of floats, 512 B of bf16) instead of 16 or 32 bytes of 64 rows.  bf16
-// values are widened exactly and rounded to nearest even once.  Both
-// contraction cores end with a barrier, so the staging slots are free here.
+// of floats, 512 B of bf16) instead of 16 or 32 bytes of 64 rows.  A wave
+// handles its rows in four batches of 16 (two per half); the old values of a
+// batch are loaded one batch ahead (those of the first batch before the
+// accumulators are staged), so their latency overlaps the staging and the
+// previous batch's adds and stores.  bf16 values are widened exactly and
+// rounded to nearest even once.  Both contraction cores end with a barrier,
+// so the staging slots are free here.
 template <bool SRC_BF16, bool DST_BF16, bool SRC_MAPPED = false>
 __device__ __forceinline__ void grad_epilogue_rows(const f32x16 (&acc)[4][4], bool src_on,
                                                    __amdgpu_buffer_rsrc_t rsS,
@@ -875,15 +879,55 @@ __device__ __forceinline__ void grad_epilogue_rows(const f32x16 (&acc)[4][4], bo
                                                    int row0, int rvalid, int D, int td,
                                                    char* lds) {
   constexpr int SES = SRC_BF16 ? 2 : 4, DES = DST_BF16 ? 2 : 4;
-  constexpr int R = 16;   // rows in flight per wave
+  constexpr int R = 16;   // rows of one batch
   using Old = std::conditional_t<SRC_BF16, u32x2, f32x4>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int wm = wave >> 1, wn = wave & 1;
   const int dcol = td * kTile + lane * 4;   // this lane's 4 columns
   const bool dok = dcol < D;
+  // batch n = 2 half + b: tile rows half * 128 + wave * 32 + b * R + k
+  auto issue = [&](int n, uint32_t (&od)[R], Old (&old)[R]) {
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+    for (int k = 0; k < R; ++k) {
+      const int trow = (n >> 1) * 128 + wave * 32 + (n & 1) * R + k;   // row within the tile
+      const bool rok = row0 + trow < rvalid, ok = rok && dok;
+      const int64_t orow = map ? (rok ? (int64_t)map[trow] : 0) : trow;   // uniform per wave
+      const uint32_t os = ok ? (uint32_t)(((SRC_MAPPED ? orow : (int64_t)trow) * D + dcol) * SES)
+                             : kOob;
+      od[k] = ok ? (uint32_t)((orow * D + dcol) * DES) : kOob;
+      if constexpr (SRC_BF16)
+        old[k] = src_on ? __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                        rsS, os, 0, 0))
+                        : u32x2{0u, 0u};
+      else
+        old[k] = src_on ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rsS, os, 0, 0))
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto finish = [&](int n, const uint32_t (&od)[R], const Old (&old)[R]) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int rl = wave * 32 + (n & 1) * R + k;   // row within the half
+      f32x4 o;
+      if constexpr (SRC_BF16)   // element d in the low half of a dword
+        o = f32x4{__builtin_bit_cast(float, old[k][0] << 16),
+                  __builtin_bit_cast(float, old[k][0] & 0xffff0000u),
+                  __builtin_bit_cast(float, old[k][1] << 16),
+                  __builtin_bit_cast(float, old[k][1] & 0xffff0000u)};
+      else
+        o = old[k];
+      const f32x4 v =
+          *reinterpret_cast<const f32x4*>(lds + rl * 1024 + ((lane ^ (rl & 31)) * 16)) + o;
+      if constexpr (DST_BF16)
+        __builtin_amdgcn_raw_buffer_store_b64(
+            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rsD, od[k], 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsD, od[k], 0, 0);
+    }
+  };
+  auto stage = [&](int half) {
     if (wn == half) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -899,49 +943,21 @@ __device__ __forceinline__ void grad_epilogue_rows(const f32x16 (&acc)[4][4], bo
           }
     }
     __syncthreads();
-#pragma unroll
-    for (int b = 0; b < 32 / R; ++b) {
-      uint32_t od[R];
-      Old old[R];
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const int trow = half * 128 + wave * 32 + b * R + k;   // row within the tile
-        const bool rok = row0 + trow < rvalid, ok = rok && dok;
-        const int64_t orow = map ? (rok ? (int64_t)map[trow] : 0) : trow;   // uniform per wave
-        const uint32_t os = ok ? (uint32_t)(((SRC_MAPPED ? orow : (int64_t)trow) * D + dcol) * SES)
-                               : kOob;
-        od[k] = ok ? (uint32_t)((orow * D + dcol) * DES) : kOob;
-        if constexpr (SRC_BF16)
-          old[k] = src_on ? __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                          rsS, os, 0, 0))
-                          : u32x2{0u, 0u};
-        else
-          old[k] = src_on ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                          rsS, os, 0, 0))
-                          : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const int rl = wave * 32 + b * R + k;                     // row within the half
-        f32x4 o;
-        if constexpr (SRC_BF16)   // element d in the low half of a dword
-          o = f32x4{__builtin_bit_cast(float, old[k][0] << 16),
-                    __builtin_bit_cast(float, old[k][0] & 0xffff0000u),
-                    __builtin_bit_cast(float, old[k][1] << 16),
-                    __builtin_bit_cast(float, old[k][1] & 0xffff0000u)};
-        else
-          o = old[k];
-        const f32x4 v =
-            *reinterpret_cast<const f32x4*>(lds + rl * 1024 + ((lane ^ (rl & 31)) * 16)) + o;
-        if constexpr (DST_BF16)
-          __builtin_amdgcn_raw_buffer_store_b64(
-              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rsD, od[k], 0, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsD, od[k], 0, 0);
-      }
-    }
-    __syncthreads();
-  }
+  };
+  uint32_t odA[R], odB[R];
+  Old oldA[R], oldB[R];
+  issue(0, odA, oldA);
+  stage(0);
+  issue(1, odB, oldB);
+  finish(0, odA, oldA);
+  issue(2, odA, oldA);
+  finish(1, odB, oldB);
+  __syncthreads();
+  stage(1);
+  issue(3, odB, oldB);
+  finish(2, odA, oldA);
+  finish(3, odB, oldB);
+  __syncthreads();
 }
 
 // Gradient tile `local` of one of the band's two contractions (is_h: dH^T).

@@ -172,6 +172,57 @@ def summarize_clock(d, out, cmds):
     print("\n".join(lines))
 
 
+def summarize_sq(dirs, out, cmds):
+    """Per-dispatch averages of SQ counters (rocprofv3 --pmc runs, one or more
+    passes) for the forward and the backward band launches, with the ratios
+    used to read them: cycles waiting on a memory counter, waiting to issue,
+    issuing, and MFMA-busy (per SIMD, so over 4 x the CU-busy cycles)."""
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for d in dirs:
+        for r in _pmc_rows(d):
+            name = r["Kernel_Name"]
+            k = ("fwd_lse_kernel" if "fwd_lse_kernel" in name else
+                 DOMINANT.split("<")[0] if DOMINANT in name.replace("void ", "").replace("flce::", "")
+                 else None)
+            if k is None:
+                continue
+            per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+            disp[(k, d)].add(r["Dispatch_Id"])
+    lines = ["# SQ counters of the forward and the backward band launches (bf16, filter off),",
+             "# 8192 x 2048 x 151552 bf16, mean, 5% ignored; per-dispatch averages.",
+             "# Commands (run from the repository root on one MI355X):"]
+    lines += [f"#   {c}" for c in cmds]
+    for k, cs in per.items():
+        n = {}
+        for (kk, d), ids in disp.items():
+            if kk == k:
+                n[d] = len(ids)
+        nd = max(n.values())
+        avg = {c: v / nd for c, v in cs.items()}
+        lines += ["", f"## {k} ({nd} dispatches per pass)", "", "| counter | per dispatch |",
+                  "|---|---|"]
+        lines += [f"| {c} | {v:.4g} |" for c, v in sorted(avg.items())]
+        wc = avg.get("SQ_WAVE_CYCLES")
+        if wc:
+            lines += ["", "| ratio | value |", "|---|---|"]
+            for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_LDS"):
+                if c in avg:
+                    lines.append(f"| {c} / SQ_WAVE_CYCLES | {avg[c] / wc:.3f} |")
+        bc = avg.get("SQ_BUSY_CU_CYCLES")
+        if bc and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            lines.append(f"| SQ_VALU_MFMA_BUSY_CYCLES / (4 SQ_BUSY_CU_CYCLES) | "
+                         f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * bc):.3f} |")
+        if bc:
+            for c in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM"):
+                if c in avg:
+                    lines.append(f"| {c} / SQ_BUSY_CU_CYCLES | {avg[c] / bc:.3f} |")
+    with open(out, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_trace(d, out, title, cmd, bench_json=None):
     import csv
     stats = trace = None
@@ -237,6 +288,7 @@ def parse():
                                                          "CAL_WRITE_DIR"))
     p.add_argument("--summarize-trace", metavar="DIR")
     p.add_argument("--summarize-clock", metavar="DIR")
+    p.add_argument("--summarize-sq", nargs="+", metavar="DIR")
     p.add_argument("--cal-bytes", type=int, default=1 << 30)
     p.add_argument("--out")
     p.add_argument("--title", default="")
@@ -300,6 +352,9 @@ def main():
         return
     if args.summarize_clock:
         summarize_clock(args.summarize_clock, args.out, args.cmd)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, args.out, args.cmd)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, args.title, " ".join(args.cmd),

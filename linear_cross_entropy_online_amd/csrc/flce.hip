@@ -244,8 +244,12 @@ template <class F>
 int launch(int cls, bool prof, hipStream_t s, F&& f) {
   hipEvent_t a = nullptr, b = nullptr;
   if (prof) {
-    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return FLCE_E_DEVICE;
-    if (hipEventRecord(a, s) != hipSuccess) return FLCE_E_DEVICE;
+    if (hipEventCreate(&a) != hipSuccess) return FLCE_E_DEVICE;
+    if (hipEventCreate(&b) != hipSuccess || hipEventRecord(a, s) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      if (b) (void)hipEventDestroy(b);
+      return FLCE_E_DEVICE;
+    }
   }
   f();
   const hipError_t e = hipGetLastError();
@@ -741,9 +745,9 @@ const char* flce_strerror(int code) {
 int flce_profile_reset(void) {
   std::lock_guard<std::mutex> g(g_prof_mu);
   for (auto& r : g_prof_pending) {
-    hipEventSynchronize(r.b);
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventSynchronize(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_prof_pending.clear();
   for (int k = 0; k < FLCE_K_COUNT; ++k) {
@@ -757,16 +761,24 @@ int flce_profile_read(int kernel_class, int64_t* launches, double* total_ms) {
   if (kernel_class < 0 || kernel_class >= FLCE_K_COUNT) return FLCE_E_UNSUPPORTED;
   if (!launches || !total_ms) return FLCE_E_NULL;
   std::lock_guard<std::mutex> g(g_prof_mu);
-  for (auto& r : g_prof_pending) {
-    if (hipEventSynchronize(r.b) != hipSuccess) return FLCE_E_DEVICE;
+  // records are consumed in order; on an error the ones not yet read stay
+  // pending (and are read or released by a later call)
+  size_t done = 0;
+  int rc = FLCE_OK;
+  for (; done < g_prof_pending.size(); ++done) {
+    const ProfRec& r = g_prof_pending[done];
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return FLCE_E_DEVICE;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      rc = FLCE_E_DEVICE;
+      break;
+    }
     g_prof_count[r.cls] += 1;
     g_prof_ms[r.cls] += ms;
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
-  g_prof_pending.clear();
+  g_prof_pending.erase(g_prof_pending.begin(), g_prof_pending.begin() + done);
+  if (rc != FLCE_OK) return rc;
   *launches = g_prof_count[kernel_class];
   *total_ms = g_prof_ms[kernel_class];
   return FLCE_OK;

@@ -161,11 +161,11 @@ size_t layout(Plan& p) {
   return o;
 }
 
-// Smallest multiple of 256 that splits n into as few parts as parts of at
-// most `cap` (a multiple of 256) would.
-int64_t even_split(int64_t n, int64_t cap) {
+// Smallest multiple of g that splits n into as few parts as parts of at
+// most `cap` (a multiple of g) would.
+int64_t even_split(int64_t n, int64_t cap, int64_t g = 256) {
   for (int64_t parts = cdiv(n, cap);; ++parts) {
-    const int64_t sz = cdiv(cdiv(n, parts), 256) * 256;
+    const int64_t sz = cdiv(cdiv(n, parts), g) * g;
     if (sz <= cap) return sz;
   }
 }
@@ -192,8 +192,18 @@ int make_plan(const flce_desc* d, Plan& p) {
   // rows) down by halves, VS is the widest multiple of 256 that fits; the
   // first NS whose VS is at least NS / 2 is taken.
   const uint64_t budget = d->ws_budget_bytes ? d->ws_budget_bytes : kDefaultBudget;
+  // VS granularity: 64 vocabulary rows for bf16 inputs without the filter (a
+  // band's last vocabulary tile may then be partial: its dZ stores and the
+  // contractions' reads stop at the band's row stride), so that the dZ
+  // buffers can use the budget to within 64 rows -- at 8192 x 2048 x 151552
+  // this makes the band 4096 x 4032 and gives every CU one gradient tile and
+  // one dZ tile per launch.  256 (whole tiles) with the filter, whose
+  // one-product placements drop a K step for 256-wide groups of 64 x 64
+  // blocks anchored at vocabulary row 0, and for fp32 inputs.
+  const bool fine = p.dtype == FLCE_BF16 && !(d->filter_eps > 0.f);
+  const int g = fine ? kFilterBlock : flce::kTile;
   const int vs_cap = int(std::min<int64_t>(p.sort ? kMaxBandVocabSorted : kMaxBandVocab,
-                                           cdiv(p.V, 256) * 256));
+                                           cdiv(p.V, g) * g));
   auto fits = [&](int ns, int vs) {
     p.NS = ns;
     p.VS = vs;
@@ -205,7 +215,7 @@ int make_plan(const flce_desc* d, Plan& p) {
   int ns_best = 0, vs_best = 0;
   for (int ns = int(std::min<int64_t>(kMaxBandRows, Npad));; ns = std::max(256, ns / 2 / 256 * 256)) {
     int vs = vs_cap;
-    while (vs > 256 && !fits(ns, vs)) vs -= 256;
+    while (vs > 256 && !fits(ns, vs)) vs -= g;
     if (fits(ns, vs) && (vs >= ns / 2 || vs == vs_cap || ns == 256)) {
       ns_best = ns;
       vs_best = vs;
@@ -219,7 +229,7 @@ int make_plan(const flce_desc* d, Plan& p) {
   // Band sizes spread evenly over the fewest bands whose rounded size still
   // fits (no thin last band); never larger than what was fitted.
   p.NS = int(even_split(std::max<int64_t>(p.N, 1), p.NS));
-  p.VS = int(even_split(p.V, p.VS));
+  p.VS = int(even_split(p.V, p.VS, g));
   p.frows = p.NS / kFilterBlock;
   p.fcols = p.VS / kFilterBlock;
   p.NF = forward_rows(p, Npad);

@@ -530,7 +530,7 @@ __global__ void clear_status_kernel(Header* __restrict__ hdr, float* __restrict_
 struct BandArgs {
   int nb0, ns_cur;   // first token row of the band, rows in it
   int vb0, vs_cur;   // first vocabulary row of the band, rows in it
-  int ldz;           // row stride of the dZ band (elements) == VS
+  int ldz;           // row stride of the dZ band (elements) == VS, a multiple of 64
   int frows, fcols;  // filter-flag grid of the band (64x64 blocks)
 };
 
@@ -749,15 +749,18 @@ __device__ __forceinline__ void dz_tile(const DzArgs<T>& a, int t, char* lds) {
   }
   if constexpr (sizeof(T) == 2) {
     // The tile's 128 KiB of bf16 dZ from LDS to the band: wave w stores rows
-    // 64 w .. 64 w + 63, two whole 512-byte rows per instruction.
+    // 64 w .. 64 w + 63, two whole 512-byte rows per instruction.  The band's
+    // row stride is a multiple of 64 columns, not necessarily of the tile:
+    // 16-byte chunks past it belong to the next row and are not written.
     __syncthreads();
     const int half = lane >> 5, ch = lane & 31;
     T* base = dz + (int64_t)(n0 - band.nb0) * band.ldz + (v0 - band.vb0);
+    const bool cin = (v0 - band.vb0) + ch * 8 < band.ldz;
 #pragma unroll 8
     for (int s2 = 0; s2 < 32; ++s2) {
       const int r = 64 * wave + 2 * s2 + half;
       const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * 512 + ((ch ^ (r & 31)) * 16));
-      *reinterpret_cast<u32x4*>(base + (int64_t)r * band.ldz + ch * 8) = v;
+      if (cin) *reinterpret_cast<u32x4*>(base + (int64_t)r * band.ldz + ch * 8) = v;
     }
   }
 }
@@ -994,7 +997,9 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
     out = dH + (int64_t)band.nb0 * D;
     rvalid = COMPACT ? nrows : band.ns_cur;
     beta = beta_h;
-    const int kpad = (band.vs_cur + kTile - 1) / kTile * kTile;
+    // K read up to the tile multiple (zeros past V in the last band), but
+    // never past the band's row stride
+    const int kpad = min((band.vs_cur + kTile - 1) / kTile * kTile, band.ldz);
     const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T3n * kTile, kpad};
     if constexpr (SORT) {
       static_assert(FILTER, "the vocabulary order only serves the filter");
@@ -1027,7 +1032,8 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
       gather_table(table, a.rowmap + band.nb0, K, half);
       const Operand A{reinterpret_cast<const char*>(H), D, D, K,
                       reinterpret_cast<const int*>(table), half};
-      const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2n * kTile, K};
+      const Operand B{reinterpret_cast<const char*>(dz), band.ldz,
+                      min((int64_t)T2n * kTile, (int64_t)band.ldz), K};
       if constexpr (FILTER) {
         const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols, !a.skip_w, 0, 0, a.kblk};
         tile_contract<T, true, true, SkipRowsOfFlags<step_k<T>()>, true>(A, B, td * kTile,
@@ -1039,7 +1045,8 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
       }
     } else {
       const Operand A{reinterpret_cast<const char*>(H + (int64_t)band.nb0 * D), D, D, band.ns_cur};
-      const Operand B{reinterpret_cast<const char*>(dz), band.ldz, (int64_t)T2n * kTile, band.ns_cur};
+      const Operand B{reinterpret_cast<const char*>(dz), band.ldz,
+                      min((int64_t)T2n * kTile, (int64_t)band.ldz), band.ns_cur};
       if constexpr (FILTER) {
         const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols, !a.skip_w, 0, 0, a.kblk};
         tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, act, acc, lds);

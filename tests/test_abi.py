@@ -160,7 +160,9 @@ def test_workspace_within_64_mib(name, N, D, V, dt):
     assert p["ws_bytes"] <= 64 * MiB
     assert p["ws_bytes"] == L.flce_workspace_bytes(N, D, V, torch.bfloat16 if dt == "bf16"
                                                    else torch.float32)
-    assert p["band_rows"] % 256 == 0 and p["band_vocab"] % 256 == 0
+    # vocabulary bands: multiples of 64 rows for bf16 without the filter,
+    # whole 256-row tiles otherwise
+    assert p["band_rows"] % 256 == 0 and p["band_vocab"] % (64 if dt == "bf16" else 256) == 0
     assert p["n_bands_rows"] * p["band_rows"] >= N and p["n_bands_vocab"] * p["band_vocab"] >= V
     assert p["fwd_band_rows"] % 256 == 0 and p["fwd_band_rows"] >= 256
 
@@ -181,9 +183,19 @@ def test_bf16_gradient_plan_within_64_mib(name, N, D, V):
     assert p["ws_bytes"] <= q["ws_bytes"] + 4 * MiB
 
 
+def test_plan_at_the_large_vocab_shape():
+    """The two dZ buffers take the budget to within 64 vocabulary rows: a
+    4096 x 4032 band, so a launch holds 256 gradient tiles and 256 dZ tiles."""
+    p = L.flce_plan(8192, 2048, 151552)
+    assert (p["band_rows"], p["band_vocab"], p["n_bands_rows"], p["n_bands_vocab"]) == \
+        (4096, 4032, 2, 38)
+    assert p["ws_bytes"] <= 64 * MiB
+    assert L.flce_plan(8192, 2048, 151552, filter_eps=2.0 ** -12)["band_vocab"] == 3840
+
+
 def test_bf16_gradient_plan_at_the_large_vocab_shape():
     p = L.flce_plan(8192, 2048, 151552, flags=_abi.FLCE_FLAG_BF16_GRADS)
-    assert (p["band_rows"], p["band_vocab"], p["n_bands_rows"]) == (4096, 3840, 2)
+    assert (p["band_rows"], p["band_vocab"], p["n_bands_rows"]) == (4096, 4032, 2)
 
 
 def test_budget_shrinks_bands_and_reports_overflow():
@@ -217,7 +229,9 @@ def test_missing_library_fails_loudly(monkeypatch):
 def test_planner_invariants_over_random_problems():
     """Seeded random shapes, dtypes, flag sets and budgets: every plan the
     library returns is within its budget, covers the problem with bands of
-    whole 256-wide tiles, and reports sizes that agree with each other; every
+    whole 256-wide tiles (64-row vocabulary bands for bf16 without the
+    filter), and
+    reports sizes that agree with each other; every
     refusal is one of the documented codes."""
     import random
 
@@ -251,7 +265,8 @@ def test_planner_invariants_over_random_problems():
         sort = bool(flags & _abi.FLCE_FLAG_SORT_VOCAB) and eps > 0
         assert info.ws_bytes == lib.flce_workspace_bytes(ctypes.byref(d))
         assert info.ws_bytes <= (budget or 64 * MiB)
-        assert info.band_rows % 256 == 0 and info.band_vocab % 256 == 0
+        coarse = dt == torch.float32 or eps > 0
+        assert info.band_rows % 256 == 0 and info.band_vocab % (256 if coarse else 64) == 0
         assert info.band_vocab <= (4096 if sort else 8192)
         assert info.n_bands_rows * info.band_rows >= max(N, 1)
         assert (info.n_bands_rows - 1) * info.band_rows < max(N, 1)

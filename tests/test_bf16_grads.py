@@ -49,7 +49,7 @@ def _ulp_bf16(x):
 
 # budgets that give one, two and many vocabulary bands per token band: the
 # four ways a dH tile ends (stage store / add / add + round / round only)
-@pytest.mark.parametrize("budget,nbv", [(0, "one"), (1 << 20, "many"), (3 << 19, "two")])
+@pytest.mark.parametrize("budget,nbv", [(0, "one"), (1 << 20, "many"), (9 << 17, "two")])
 def test_bf16_grads_fused_ragged(budget, nbv):
     N, D, V = 1500, 264, 3000
     H, W, y = fi.random_case(N, D, V, seed=51, sigma_w=0.05, ignore_frac=0.05)
@@ -67,9 +67,12 @@ def test_bf16_grads_fused_ragged(budget, nbv):
 def test_bf16_grads_round_once_structure():
     """dH is the float sum rounded once: within one bf16 spacing of the float
     path's dH (the two sum in different band orders, so a value next to a
-    rounding boundary may round the other way).  With one token band dW is
-    rounded once too; with R token bands each rounding moves dW by at most
-    half a spacing of the running sum."""
+    rounding boundary may round the other way).  The float sums of the two
+    orders differ by fp32 rounding, which is negligible next to the bf16
+    spacing except for values that are small next to their row (cancellation):
+    those are held to one spacing of 1/64 of the row's largest |dH| instead of
+    their own.  With one token band dW is rounded once too; with R token bands
+    each rounding moves dW by at most half a spacing of the running sum."""
     N, D, V = 1100, 264, 9000
     H, W, y = fi.random_case(N, D, V, seed=52, sigma_w=0.05, ignore_frac=0.05)
     Hd, Wd, yd = _dev(H, W, y)
@@ -82,7 +85,8 @@ def test_bf16_grads_round_once_structure():
         for i in range(3):
             assert torch.equal(f[i], b[i])
         dH32, dW32 = f[3].double(), f[4].double()
-        eH = (b[3].double() - dH32).abs() / _ulp_bf16(f[3])
+        floor = dH32.abs().amax(1, keepdim=True).expand_as(dH32) / 64
+        eH = (b[3].double() - dH32).abs() / _ulp_bf16(torch.maximum(dH32.abs(), floor))
         # unit: the spacing at twice the row's largest |dW| (a running sum of
         # token bands may exceed the final value)
         eW = (b[4].double() - dW32).abs() / _ulp_bf16(2 * dW32.abs().amax(1, keepdim=True)

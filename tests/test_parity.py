@@ -175,13 +175,25 @@ def test_deterministic_bits():
         assert torch.equal(x, z)
 
 
+def _same_bands(N, D, V, **kw):
+    """The filtered call's bands equal the unfiltered call's (whole-tile
+    bands with the filter, 64-row bands without: equal for this V)."""
+    a = L.flce_plan(N, D, V, flags=kw.get("flags", 0) & L.FLCE_FLAG_BF16_GRADS)
+    b = L.flce_plan(N, D, V, **kw)
+    keys = ("band_rows", "band_vocab", "n_bands_rows", "n_bands_vocab")
+    assert all(a[k] == b[k] for k in keys), (a, b)
+
+
 def test_filter_matches_filtered_oracle():
     """eps = 2^-12 on 64 x 64 blocks against the oracle's filtered mode; a
     vanishing eps drops nothing and equals the unfiltered result bit for bit."""
-    # softmax ~ 1/V < eps needs V > 4096; logit std 0.4 keeps most blocks below eps
-    H, W, y = fi.random_case(640, 128, 20000, seed=28, sigma_w=0.4 / math.sqrt(128))
+    # softmax ~ 1/V < eps needs V > 4096; logit std 0.4 keeps most blocks below eps.
+    # V = 78 x 256: the filter's whole-tile bands and the unfiltered 64-row
+    # bands come out the same, so the two sum in the same order
+    H, W, y = fi.random_case(640, 128, 19968, seed=28, sigma_w=0.4 / math.sqrt(128))
     Hd, Wd, yd = _dev(H, W, y)
     eps = 2.0 ** -12
+    _same_bands(640, 128, 19968, filter_eps=eps)
     base = L.flce_fused_fwd_bwd(Hd, Wd, yd)
     tiny = L.flce_fused_fwd_bwd(Hd, Wd, yd, filter_eps=1e-30)
     for x, z in zip(base, tiny):
@@ -203,7 +215,7 @@ def test_filter_on_one_product(mode):
     drops a 64-wide K step when its tile's 256 rows (dH) or 256 vocabulary
     rows (dW) are all dropped there, i.e. filter blocks of 256 x 64 (dH) and
     64 x 256 (dW), against the oracle's one-product filter."""
-    H, W, y = fi.random_case(640, 128, 20000, seed=28, sigma_w=0.4 / math.sqrt(128))
+    H, W, y = fi.random_case(640, 128, 19968, seed=28, sigma_w=0.4 / math.sqrt(128))
     Hd, Wd, yd = _dev(H, W, y)
     eps = 2.0 ** -12
     full_c = mode.startswith("full_c")
@@ -211,6 +223,7 @@ def test_filter_on_one_product(mode):
     products, block = ("dH", (256, 64)) if full_c else ("dW", (64, 256))
     if mode.endswith("bf16_grads"):
         flags |= L.FLCE_FLAG_BF16_GRADS
+    _same_bands(640, 128, 19968, filter_eps=eps, flags=flags)
     base = L.flce_fused_fwd_bwd(Hd, Wd, yd, flags=flags & L.FLCE_FLAG_BF16_GRADS)
     out = L.flce_fused_fwd_bwd(Hd, Wd, yd, filter_eps=eps, flags=flags)
     ref = O.linear_cross_entropy(H, W, y, filter_eps=eps, filter_block=block,

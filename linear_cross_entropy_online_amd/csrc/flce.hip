@@ -189,7 +189,7 @@ int make_plan(const flce_desc* d, Plan& p) {
   // The band is as large as the budget allows: every band costs a launch,
   // and the fp32 read-modify-write of dH and dW per step scales with
   // 1 / NS + 1 / VS.  For NS from its cap (its tiles fill the machine at 4096
-  // rows) down by halves, VS is the widest multiple of 256 that fits; the
+  // rows) down by halves, VS is the widest multiple of g (below) that fits; the
   // first NS whose VS is at least NS / 2 is taken.
   const uint64_t budget = d->ws_budget_bytes ? d->ws_budget_bytes : kDefaultBudget;
   // VS granularity: 64 vocabulary rows for bf16 inputs without the filter (a

@@ -64,6 +64,26 @@ def test_bf16_grads_fused_ragged(budget, nbv):
     assert torch.all(out[3][ign] == 0)
 
 
+def test_bf16_grads_partial_last_vocab_tile():
+    """bf16 gradients with vocabulary bands that are not a multiple of the
+    tile (each band's last vocabulary tile partial), several bands both ways."""
+    N, D, V = 1100, 264, 3000
+    for b in range(256 << 10, 8 << 20, 32 << 10):
+        try:
+            plan = L.flce_plan(N, D, V, flags=B, ws_budget_bytes=b)
+        except L.FlceError:
+            continue
+        if plan["band_vocab"] % 256 and plan["n_bands_vocab"] > 2 and plan["n_bands_rows"] > 1:
+            break
+    else:
+        raise AssertionError("no such budget")
+    H, W, y = fi.random_case(N, D, V, seed=54, sigma_w=0.05, ignore_frac=0.05)
+    ref = O.linear_cross_entropy(H, W, y, reduction="mean")
+    Hd, Wd, yd = _dev(H, W, y)
+    out = L.flce_fused_fwd_bwd(Hd, Wd, yd, flags=B, ws_budget_bytes=b)
+    _check(f"bf16g_partial_tile_{plan['band_vocab']}", out, ref)
+
+
 def test_bf16_grads_round_once_structure():
     """dH is the float sum rounded once: within one bf16 spacing of the float
     path's dH (the two sum in different band orders, so a value next to a

@@ -69,6 +69,40 @@ def test_ragged_shapes_many_bands(dt):
     _check_against_oracle(f"ragged_{dt}_default", H, W, y, out2, ref, dt)
 
 
+def _partial_tile_budget(N, D, V, flags=0):
+    """A workspace budget whose plan has several vocabulary bands of a width
+    that is not a multiple of the 256-wide tile (each band's last vocabulary
+    tile partial)."""
+    for b in range(256 << 10, 8 << 20, 32 << 10):
+        try:
+            p = L.flce_plan(N, D, V, flags=flags, ws_budget_bytes=b)
+        except L.FlceError:
+            continue
+        if p["band_vocab"] % 256 and p["n_bands_vocab"] > 2 and p["n_bands_rows"] > 1:
+            return b, p
+    raise AssertionError("no such budget")
+
+
+@pytest.mark.parametrize("compact", [False, True])
+def test_partial_last_vocab_tile_bands(compact):
+    """64-row vocabulary bands (bf16 without the filter): the band's last
+    vocabulary tile stores and is read only up to the band's row stride;
+    several bands along N and V, ragged N, D and V, against the oracle."""
+    N, D, V = 1100, 264, 3000
+    flags = L.FLCE_FLAG_COMPACT_IGNORED if compact else 0
+    budget, plan = _partial_tile_budget(N, D, V, flags)
+    H, W, y = fi.random_case(N, D, V, seed=29, sigma_w=0.05, ignore_frac=0.1)
+    ref = O.linear_cross_entropy(H, W, y, reduction="mean")
+    Hd, Wd, yd = _dev(H, W, y)
+    out = L.flce_fused_fwd_bwd(Hd, Wd, yd, flags=flags, ws_budget_bytes=budget)
+    if compact:   # the log-sum-exp of an ignored row is 0 under compaction (not computed)
+        ign = (y == fi.IGNORE_INDEX).numpy()
+        assert torch.all(out[2].cpu()[torch.from_numpy(ign)] == 0)
+        ref = dict(ref, lse=np.where(ign, 0.0, ref["lse"]))
+    _check_against_oracle(f"partial_tile_bands_{plan['band_vocab']}_c{int(compact)}", H, W, y,
+                          out, ref, "bf16")
+
+
 @pytest.mark.parametrize("reduction", ["sum", "none", "mean"])
 def test_separate_forward_backward_reductions(reduction):
     H, W, y = fi.random_case(700, 128, 2100, seed=22, sigma_w=0.08)

@@ -52,6 +52,7 @@ struct Plan {
   int NS, VS;          // backward band sizes (multiples of 256)
   int nbn, nbv;        // backward band counts
   int frows, fcols;    // flag grid of a backward band
+  int fstride;         // its row stride: fcols rounded up to a multiple of 4
   int nblk;            // combine blocks (16 rows each)
   size_t big;          // bytes shared by the forward partials and the dZ buffers
   size_t dz_bytes;     // one dZ band buffer
@@ -132,7 +133,8 @@ size_t layout(Plan& p) {
   o = align256(o + size_t(p.nblk) * 8);
   p.off_bcnt = o;
   o = align256(o + size_t(p.nblk) * 4);
-  p.flag_bytes = align256(size_t(p.frows) * p.fcols);
+  p.fstride = (p.fcols + 3) / 4 * 4;
+  p.flag_bytes = align256(size_t(p.frows) * p.fstride);
   p.off_flags = o;
   o += 2 * p.flag_bytes;
   p.off_flagsT = o;
@@ -192,15 +194,19 @@ int make_plan(const flce_desc* d, Plan& p) {
   // rows) down by halves, VS is the widest multiple of g (below) that fits; the
   // first NS whose VS is at least NS / 2 is taken.
   const uint64_t budget = d->ws_budget_bytes ? d->ws_budget_bytes : kDefaultBudget;
-  // VS granularity: 64 vocabulary rows for bf16 inputs without the filter (a
-  // band's last vocabulary tile may then be partial: its dZ stores and the
-  // contractions' reads stop at the band's row stride), so that the dZ
-  // buffers can use the budget to within 64 rows -- at 8192 x 2048 x 151552
-  // this makes the band 4096 x 4032 and gives every CU one gradient tile and
-  // one dZ tile per launch.  256 (whole tiles) with the filter, whose
-  // one-product placements drop a K step for 256-wide groups of 64 x 64
-  // blocks anchored at vocabulary row 0, and for fp32 inputs.
-  const bool fine = p.dtype == FLCE_BF16 && !(d->filter_eps > 0.f);
+  // VS granularity: 64 vocabulary rows for bf16 inputs (a band's last
+  // vocabulary tile may then be partial: its dZ stores and the contractions'
+  // reads stop at the band's row stride, and its flag columns past the band
+  // are padding that is always dropped), so that the dZ buffers can use the
+  // budget to within 64 rows -- at 8192 x 2048 x 151552 this makes the band
+  // 4096 x 4032 and gives every CU one gradient tile and one dZ tile per
+  // launch.  256 (whole tiles) for the filter on one product, which drops a K
+  // step for 256-wide groups of 64 x 64 blocks anchored at vocabulary row 0
+  // (with the filter on both products the dropped blocks are zeros and the
+  // grouping changes no value), with a sorted vocabulary, and for fp32.
+  const bool one_product = (d->flags & (FLCE_FLAG_FILTER_FULL_C | FLCE_FLAG_FILTER_FULL_E)) != 0;
+  const bool filt = d->filter_eps > 0.f;
+  const bool fine = p.dtype == FLCE_BF16 && !(filt && (one_product || p.sort));
   const int g = fine ? kFilterBlock : flce::kTile;
   const int vs_cap = int(std::min<int64_t>(p.sort ? kMaxBandVocabSorted : kMaxBandVocab,
                                            cdiv(p.V, g) * g));
@@ -385,6 +391,7 @@ flce::BandArgs band_args(const Plan& p, int k) {
   band.ldz = p.VS;
   band.frows = p.frows;
   band.fcols = p.fcols;
+  band.fstride = p.fstride;
   return band;
 }
 

@@ -532,6 +532,7 @@ struct BandArgs {
   int vb0, vs_cur;   // first vocabulary row of the band, rows in it
   int ldz;           // row stride of the dZ band (elements) == VS, a multiple of 64
   int frows, fcols;  // filter-flag grid of the band (64x64 blocks)
+  int fstride;       // row stride of the flags: fcols rounded up to a multiple of 4
 };
 
 template <typename T>
@@ -561,7 +562,7 @@ struct DzArgs {
   BandArgs band;
   int TMv, TNn;          // vocabulary and token-row tiles of the band
   T* dz;                 // the band's dZ buffer [ns][ldz]
-  uint8_t* flags;        // [frows][fcols]
+  uint8_t* flags;        // [frows][fstride]
   uint8_t* flagsT;       // [fcols][frows]
   const int* rowmap;     // row compaction: band rows are positions of rowmap (else rows)
   int keep_dropped;      // store dropped blocks' dZ too (filter on one product only)
@@ -739,8 +740,14 @@ __device__ __forceinline__ void dz_tile(const DzArgs<T>& a, int t, char* lds) {
       gk[bi][1] = kp || a.keep_dropped ? g[2 * bj + 1] : 0.f;
       if (lane == 0) {
         const int fr = fr0 + bj, fc = fc0 + bi;
-        flags[fr * band.fcols + fc] = kp ? 0 : 1;
-        flagsT[fc * band.frows + fr] = kp ? 0 : 1;
+        if (fc < band.fcols) {
+          flags[fr * band.fstride + fc] = kp ? 0 : 1;
+          flagsT[fc * band.frows + fr] = kp ? 0 : 1;
+        } else {
+          // past the band (its last tile is partial): a padding column, never
+          // the reason a K step runs
+          flags[fr * band.fstride + fc] = 1;
+        }
       }
     }
     store_block(2 * bj, p[0], gk[0][0], gk[1][0]);
@@ -1035,7 +1042,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
       const Operand B{reinterpret_cast<const char*>(dz), band.ldz,
                       min((int64_t)T2n * kTile, (int64_t)band.ldz), K};
       if constexpr (FILTER) {
-        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols, !a.skip_w, 0, 0, a.kblk};
+        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fstride, !a.skip_w, 0, 0, a.kblk};
         tile_contract<T, true, true, SkipRowsOfFlags<step_k<T>()>, true>(A, B, td * kTile,
                                                                         tr * kTile, K, act, acc,
                                                                         lds);
@@ -1048,7 +1055,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
       const Operand B{reinterpret_cast<const char*>(dz), band.ldz,
                       min((int64_t)T2n * kTile, (int64_t)band.ldz), band.ns_cur};
       if constexpr (FILTER) {
-        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fcols, !a.skip_w, 0, 0, a.kblk};
+        const SkipRowsOfFlags<step_k<T>()> act{flags + tr * 4, band.fstride, !a.skip_w, 0, 0, a.kblk};
         tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, act, acc, lds);
       } else {
         tile_contract<T, true, true>(A, B, td * kTile, tr * kTile, band.ns_cur, AllActive{}, acc,

@@ -160,8 +160,8 @@ def test_workspace_within_64_mib(name, N, D, V, dt):
     assert p["ws_bytes"] <= 64 * MiB
     assert p["ws_bytes"] == L.flce_workspace_bytes(N, D, V, torch.bfloat16 if dt == "bf16"
                                                    else torch.float32)
-    # vocabulary bands: multiples of 64 rows for bf16 without the filter,
-    # whole 256-row tiles otherwise
+    # vocabulary bands: multiples of 64 rows for bf16, whole 256-row tiles
+    # for fp32
     assert p["band_rows"] % 256 == 0 and p["band_vocab"] % (64 if dt == "bf16" else 256) == 0
     assert p["n_bands_rows"] * p["band_rows"] >= N and p["n_bands_vocab"] * p["band_vocab"] >= V
     assert p["fwd_band_rows"] % 256 == 0 and p["fwd_band_rows"] >= 256
@@ -190,7 +190,9 @@ def test_plan_at_the_large_vocab_shape():
     assert (p["band_rows"], p["band_vocab"], p["n_bands_rows"], p["n_bands_vocab"]) == \
         (4096, 4032, 2, 38)
     assert p["ws_bytes"] <= 64 * MiB
-    assert L.flce_plan(8192, 2048, 151552, filter_eps=2.0 ** -12)["band_vocab"] == 3840
+    assert L.flce_plan(8192, 2048, 151552, filter_eps=2.0 ** -12)["band_vocab"] == 4032
+    one = L.flce_plan(8192, 2048, 151552, filter_eps=2.0 ** -12, flags=_abi.FLCE_FLAG_FILTER_FULL_C)
+    assert one["band_vocab"] == 3840
 
 
 def test_bf16_gradient_plan_at_the_large_vocab_shape():
@@ -229,8 +231,8 @@ def test_missing_library_fails_loudly(monkeypatch):
 def test_planner_invariants_over_random_problems():
     """Seeded random shapes, dtypes, flag sets and budgets: every plan the
     library returns is within its budget, covers the problem with bands of
-    whole 256-wide tiles (64-row vocabulary bands for bf16 without the
-    filter), and
+    whole 256-wide tiles (64-row vocabulary bands for bf16 unless the filter
+    is on one product or sorts the vocabulary), and
     reports sizes that agree with each other; every
     refusal is one of the documented codes."""
     import random
@@ -265,7 +267,8 @@ def test_planner_invariants_over_random_problems():
         sort = bool(flags & _abi.FLCE_FLAG_SORT_VOCAB) and eps > 0
         assert info.ws_bytes == lib.flce_workspace_bytes(ctypes.byref(d))
         assert info.ws_bytes <= (budget or 64 * MiB)
-        coarse = dt == torch.float32 or eps > 0
+        one_product = flags & (_abi.FLCE_FLAG_FILTER_FULL_C | _abi.FLCE_FLAG_FILTER_FULL_E)
+        coarse = dt == torch.float32 or (eps > 0 and (one_product or sort))
         assert info.band_rows % 256 == 0 and info.band_vocab % (256 if coarse else 64) == 0
         assert info.band_vocab <= (4096 if sort else 8192)
         assert info.n_bands_rows * info.band_rows >= max(N, 1)

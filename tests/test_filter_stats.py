@@ -66,10 +66,12 @@ def _expected(kept, N, nvalid, D, V, plan, products):
                                     for b in range(nb))
             if products in ("both", "dW"):
                 K = max(nrows, 0)
+                vb = _cdiv(vs, BLK)   # the band's vocabulary blocks (a tile may reach past them)
                 for tv in range(_cdiv(vs, TILE)):
                     nb = _cdiv(K, BLK)
                     tot += Td * nb
-                    act += Td * sum(any(k(r0 + b, c0 + 4 * tv + i) for i in range(4))
+                    act += Td * sum(any(k(r0 + b, c0 + 4 * tv + i) for i in range(4)
+                                        if 4 * tv + i < vb)
                                     for b in range(nb))
     return act, tot
 

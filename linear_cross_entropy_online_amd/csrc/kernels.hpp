@@ -896,13 +896,23 @@ __device__ __forceinline__ void grad_epilogue_rows(const f32x16 (&acc)[4][4], bo
   const int wm = wave >> 1, wn = wave & 1;
   const int dcol = td * kTile + lane * 4;   // this lane's 4 columns
   const bool dok = dcol < D;
+  // The map entries of the wave's 64 rows, one per lane (lane L: row
+  // (L / 32) 128 + 32 wave + L % 32), in one load; each row's entry is then
+  // read from its lane, not loaded on its own.
+  int mapv = 0;
+  if (map) {
+    const int r = (lane >> 5) * 128 + wave * 32 + (lane & 31);
+    mapv = row0 + r < rvalid ? map[r] : 0;
+  }
   // batch n = 2 half + b: tile rows half * 128 + wave * 32 + b * R + k
   auto issue = [&](int n, uint32_t (&od)[R], Old (&old)[R]) {
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const int trow = (n >> 1) * 128 + wave * 32 + (n & 1) * R + k;   // row within the tile
       const bool rok = row0 + trow < rvalid, ok = rok && dok;
-      const int64_t orow = map ? (rok ? (int64_t)map[trow] : 0) : trow;   // uniform per wave
+      const int64_t orow =
+          map ? (rok ? (int64_t)__builtin_amdgcn_readlane(mapv, (n >> 1) * 32 + (n & 1) * R + k) : 0)
+              : trow;   // uniform per wave
       const uint32_t os = ok ? (uint32_t)(((SRC_MAPPED ? orow : (int64_t)trow) * D + dcol) * SES)
                              : kOob;
       od[k] = ok ? (uint32_t)((orow * D + dcol) * DES) : kOob;

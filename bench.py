@@ -259,6 +259,10 @@ def summarize_trace(d, out, title, cmd, bench_json=None):
         keep = {k: b[k] for k in ("value", "ms_per_step", "mfma_util", "roofline", "peak_extra_mib")}
         lines += ["", "Same build, `bench.py` line (default arguments, separate run):", "", "```",
                   json.dumps(keep), "```"]
+        if keep["roofline"] and keep["roofline"].get("traffic") is None and stored_traffic():
+            lines += ["", "(`traffic` is null in that line because the counters of the same "
+                      "measurement pass were summarised after it; they are in "
+                      f"`{os.path.basename(TRAFFIC_FILE)}`: {stored_traffic():.0f} bytes per launch.)"]
     with open(out, "w") as fo:
         fo.write("\n".join(lines) + "\n")
     print("\n".join(lines))

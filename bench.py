@@ -301,6 +301,16 @@ def parse():
     return p.parse_args()
 
 
+def data_label(wl):
+    """What the seeded inputs of a workload are, from its recipe."""
+    tg = "uniform targets" if wl.targets == "uniform" else f"Zipf({wl.zipf_s:g}) targets"
+    parts = [f"seeded N(0,1) H, N(0,{wl.sigma_w:g}^2) W, {tg}",
+             f"{100 * wl.ignore_frac:g}% ignore_index", f"{wl.reduction} reduction"]
+    if wl.peaked:
+        parts.append("+8 target logit on 90% of rows")
+    return "synthetic (" + ", ".join(parts) + ")"
+
+
 def backward_flops_by_class(plan, N, D, V, serial=False):
     """Algorithmic flops of the backward launch classes, following the
     library's launch sequence: launch k holds the dZ tiles of band k
@@ -503,7 +513,7 @@ def main():
         "metric": METRIC, "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": wl.dtype, "data": "synthetic (seeded N(0,1) H, N(0,0.02^2) W, uniform targets)",
+        "dtype": wl.dtype, "data": data_label(wl),
         "config": {"workload": wl.name, "N": N, "D": D, "V": V, "reduction": wl.reduction,
                    "ignore_frac": wl.ignore_frac, "filter_eps": args.filter_eps,
                    "compact_ignored": bool(args.compact_ignored),

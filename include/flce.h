@@ -173,10 +173,17 @@ typedef struct flce_plan_info {
 } flce_plan_info;
 
 /* Exact workspace size for *d (the maximum over the three compute entry
- * points); 0 if *d is invalid. */
+ * points); 0 if *d is invalid.  The library's own call, no passage of the
+ * pages behind it: it states the O(N + band) scratch the path needs in place
+ * of the [N, V] logits that the pages' chunked and SRAM-tiled designs avoid
+ * materialising (Trillion Labs notes, section "1. Chunked Cross-Entropy";
+ * CCE Sec. 4, the logits never stored in global memory).  Pure host
+ * arithmetic: touches no device. */
 size_t flce_workspace_bytes(const flce_desc* d);
 
-/* Fills *out with the plan for *d.  Returns FLCE_OK or an argument error. */
+/* Fills *out with the plan for *d (the library's own call: the band sizes
+ * behind flce_workspace_bytes).  Returns FLCE_OK or an argument error
+ * (FLCE_E_NULL for a NULL out).  Pure host arithmetic: touches no device. */
 int flce_plan(const flce_desc* d, flce_plan_info* out);
 
 /* Forward: loss_rows [N], lse [N] (every row, ignored ones included) and,
@@ -202,7 +209,13 @@ int flce_backward(const flce_desc* d, const void* H, const void* W, const int64_
                   void* dH, void* dW,
                   void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Forward then backward with an upstream gradient of 1, in one call. */
+/* Forward then backward with an upstream gradient of 1, in one call: the
+ * loss and both gradients of the same definitions as flce_forward and
+ * flce_backward (Trillion Labs notes, section "Cross Entropy를 다시 보면";
+ * PyTorch 2.13 chapter, section "먼저 수식에서 없앨 수 있는 tensor를
+ * 찾는다"; CCE Alg. 2 then Alg. 4).  Arguments as in those two; loss may be
+ * NULL iff reduction == FLCE_NONE; dH may be NULL only when N == 0.  With
+ * N == 0 the call sets loss to 0 and dW to 0.  Errors as in those two. */
 int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const int64_t* y,
                        float* loss_rows, float* lse, float* loss,
                        void* dH, void* dW,
@@ -224,7 +237,11 @@ int flce_scale_gradients(const flce_desc* d, const float* dloss, void* dH, void*
                          hipStream_t stream);
 
 /* Synchronises `stream`, then reads the status word of `ws` into *out
- * (bit 0: a target outside [0, V) that is not ignore_index). */
+ * (bit 0: a target outside [0, V) that is not ignore_index).  The library's
+ * own call: the pages define no error channel; it reports the reading that
+ * only ignore_index may fall outside [0, V) (Trillion Labs notes, section
+ * "1. Chunked Cross-Entropy", where ignored rows are masked out).  Returns
+ * FLCE_E_NULL for a NULL argument, FLCE_E_DEVICE if a HIP call fails. */
 int flce_device_status(const void* ws, hipStream_t stream, int32_t* out);
 
 /* Work the gradient filter left out (CCE Sec. 4.3, "Gradient filtering",
@@ -241,7 +258,7 @@ int flce_device_status(const void* ws, hipStream_t stream, int32_t* out);
  * FLCE_E_NULL for a NULL argument, FLCE_E_DEVICE if a HIP call fails. */
 int flce_filter_stats(const void* ws, hipStream_t stream, int64_t* active, int64_t* total);
 
-/* Static description of a return code. */
+/* Static description of a return code (the library's own call); never NULL. */
 const char* flce_strerror(int code);
 
 /* Kernel classes reported by flce_profile_read. */
@@ -260,15 +277,19 @@ enum {
   FLCE_K_COUNT = 7
 };
 
-/* Launch timing recorded while desc->flags has FLCE_FLAG_PROFILE.  Each
+/* The library's own calls, for measurement (no passage of the pages).
+ * Launch timing recorded while desc->flags has FLCE_FLAG_PROFILE.  Each
  * launch made under the flag is bracketed by two HIP events on the launch
  * stream.  flce_profile_read synchronises those events and returns, for
  * kernel class k, the number of launches and their summed duration in ms
  * since the last flce_profile_reset. */
 int flce_profile_reset(void);
 int flce_profile_read(int kernel_class, int64_t* launches, double* total_ms);
+/* flce_profile_read returns FLCE_E_UNSUPPORTED for an unknown class,
+ * FLCE_E_NULL for a NULL output and FLCE_E_DEVICE if an event read fails
+ * (the unread records stay pending). */
 
-/* Library version, e.g. "flce 0.1.0 gfx950". */
+/* Library version, e.g. "flce 0.1.0 gfx950" (the library's own call). */
 const char* flce_version(void);
 
 #ifdef __cplusplus

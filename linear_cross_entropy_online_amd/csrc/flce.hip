@@ -270,7 +270,11 @@ int launch(int cls, bool prof, hipStream_t s, F&& f) {
   f();
   const hipError_t e = hipGetLastError();
   if (prof) {
-    if (hipEventRecord(b, s) != hipSuccess) return FLCE_E_DEVICE;
+    if (hipEventRecord(b, s) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      (void)hipEventDestroy(b);
+      return FLCE_E_DEVICE;
+    }
     std::lock_guard<std::mutex> g(g_prof_mu);
     g_prof_pending.push_back({cls, a, b});
   }
@@ -701,17 +705,20 @@ int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const i
 
 int flce_scale_gradients(const flce_desc* d, const float* dloss, void* dH, void* dW,
                          hipStream_t stream) {
-  Plan p;
-  FLCE_TRY(make_plan(d, p));
+  // only the descriptor's arguments are checked: the scaling needs no
+  // workspace, so no band plan is made
+  FLCE_TRY(validate(d));
   if (d->reduction == FLCE_NONE) return FLCE_E_UNSUPPORTED;
-  if (!dW || (p.N > 0 && !dH)) return FLCE_E_NULL;
+  const int64_t N = d->n_rows, D = d->hidden, V = d->vocab;
+  const bool bf16g = (d->flags & FLCE_FLAG_BF16_GRADS) != 0;
+  if (!dW || (N > 0 && !dH)) return FLCE_E_NULL;
   if (!aligned(dW, 16) || (dH && !aligned(dH, 16)) || (dloss && !aligned(dloss, 4)))
     return FLCE_E_ALIGN;
   if (!dloss) return FLCE_OK;   // an upstream gradient of 1
   const bool prof = d->flags & FLCE_FLAG_PROFILE;
   auto scale = [&](void* g, int64_t n) {
     return launch(FLCE_K_AUX, prof, stream, [&] {
-      if (p.bf16g)
+      if (bf16g)
         flce::scale_bf16_kernel<<<dim3(2048), dim3(256), 0, stream>>>(static_cast<uint16_t*>(g), n,
                                                                       dloss);
       else
@@ -719,8 +726,8 @@ int flce_scale_gradients(const flce_desc* d, const float* dloss, void* dH, void*
                                                                      dloss);
     });
   };
-  if (p.N > 0) FLCE_TRY(scale(dH, p.N * p.D));
-  return scale(dW, p.V * p.D);
+  if (N > 0) FLCE_TRY(scale(dH, N * D));
+  return scale(dW, V * D);
 }
 
 int flce_filter_stats(const void* ws, hipStream_t stream, int64_t* active, int64_t* total) {

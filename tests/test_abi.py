@@ -144,6 +144,10 @@ def test_argument_errors_return_before_any_device_work():
     assert lib.flce_scale_gradients(ctypes.byref(d), ok[0], _fake(A + 8), ok[2], None) == \
         _abi.FLCE_E_ALIGN
     assert lib.flce_scale_gradients(ctypes.byref(d), None, ok[1], ok[2], None) == _abi.FLCE_OK
+    # the scaling needs no workspace: a budget the planner rejects does not stop it
+    tight = L.make_desc(8192, 2048, 151552, ws_budget_bytes=1 << 10)
+    assert lib.flce_workspace_bytes(ctypes.byref(tight)) == 0
+    assert lib.flce_scale_gradients(ctypes.byref(tight), None, ok[1], ok[2], None) == _abi.FLCE_OK
     # fused: NULL workspace
     assert lib.flce_fused_fwd_bwd(ctypes.byref(d), *ok[:3], ok[3], ok[4], ok[5], ok[0], ok[1],
                                   None, need, None) == _abi.FLCE_E_NULL

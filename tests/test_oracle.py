@@ -262,6 +262,62 @@ def test_filter_brute_force_small_blocks():
     assert 0.0 < frac < 1.0
 
 
+@pytest.mark.parametrize("block", [(4, 4), (4, 2), (2, 4)])
+def test_filter_block_stats_brute_force(block):
+    """The dropped-block fraction counted by loops over the definition (CCE
+    Alg. 4: a block is dropped iff every |softmax - onehot| of its
+    non-ignored rows is below eps; a block with no such row is dropped), and
+    equal to the share of the brute-force-pinned block maxima below eps.
+    Counting kept blocks, or a reversed comparison, gives another number."""
+    H, W, y = _case(13, 5, 19, seed=18, ignore_frac=0.3, sigma_w=3.0)
+    y[0:4] = -100
+    N, D = H.shape
+    V = W.shape[0]
+    nb, vb = block
+    eps = 0.05
+    full = O.linear_cross_entropy(H, W, y)
+    G = [[0.0] * V for _ in range(N)]
+    for n in range(N):
+        if int(y[n]) == -100:
+            continue
+        z = [sum(H[n, k] * W[v, k] for k in range(D)) for v in range(V)]
+        m = max(z)
+        lse = m + math.log(sum(math.exp(t - m) for t in z))
+        for v in range(V):
+            G[n][v] = math.exp(z[v] - lse) - (1.0 if v == y[n] else 0.0)
+    dropped = total = 0
+    for a in range(0, N, nb):
+        for b in range(0, V, vb):
+            total += 1
+            keep = any(abs(G[n][v]) >= eps
+                       for n in range(a, min(N, a + nb)) if int(y[n]) != -100
+                       for v in range(b, min(V, b + vb)))
+            dropped += 0 if keep else 1
+    want = dropped / total
+    assert 0 < dropped < total
+    got = O.filter_block_stats(H, W, y, full["lse"], eps, block=block)
+    assert got == want
+    bmax = O.filter_block_max(H, W, y, block=block, row_chunk=4)
+    assert got == float((bmax < eps).mean())
+
+
+def test_filter_block_stats_hand_counted():
+    """Three rows, four vocabulary entries, 1 x 2 blocks, eps = 1e-3; with
+    logits (10, 0, -10, -10) on every row the softmax is about (1, 4.5e-5,
+    2.1e-9, 2.1e-9):
+      row 0, target 0: |G| ~ (4.5e-5, 4.5e-5, 2e-9, 2e-9): both blocks dropped;
+      row 1, target 3: |G| ~ (1, 4.5e-5, 2e-9, 1):          both kept;
+      row 2, ignored:  no non-ignored row:                   both dropped.
+    Four of six blocks are dropped."""
+    H = np.ones((3, 1))
+    W = np.array([[10.0], [0.0], [-10.0], [-10.0]])
+    y = np.array([0, 3, -100])
+    lse = O.lse_all(H, W)
+    assert O.filter_block_stats(H, W, y, lse, 1e-3, block=(1, 2)) == 4 / 6
+    # the same rows as one 3 x 2 block per vocabulary pair: row 1 keeps both
+    assert O.filter_block_stats(H, W, y, lse, 1e-3, block=(3, 2)) == 0.0
+
+
 @pytest.mark.parametrize("products,block", [("dH", (4, 2)), ("dW", (2, 4))])
 def test_filter_one_product_brute_force(products, block):
     """CCE's FullC / FullE: the filter drops blocks from one product only; the

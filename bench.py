@@ -280,6 +280,10 @@ def parse():
     p.add_argument("--sort-vocab", action="store_true",
                    help="filter blocks over the vocabulary sorted by average logit "
                         "(FLCE_FLAG_SORT_VOCAB; needs --filter-eps)")
+    p.add_argument("--kahan", action="store_true",
+                   help="bf16 gradients with Kahan-compensated dW (flce_fused_fwd_bwd_kahan; "
+                        "implies --bf16-grads); the [V, D] bf16 compensation counts in "
+                        "total_mib_incl_outputs")
     p.add_argument("--bf16-grads", action="store_true",
                    help="dH and dW written in bf16 (FLCE_FLAG_BF16_GRADS)")
     p.add_argument("--cpu-rows", type=int, default=8192,
@@ -394,6 +398,8 @@ def main():
     H, W, y = fi.make(wl.name)
     Hd, Wd, yd = H.to(dev), W.to(dev), y.to(dev)
     N, D, V = wl.n, wl.d, wl.v
+    if args.kahan:
+        args.bf16_grads = True
     flags0 = L.FLCE_FLAG_COMPACT_IGNORED if args.compact_ignored else 0
     if args.bf16_grads:
         flags0 |= L.FLCE_FLAG_BF16_GRADS
@@ -406,7 +412,14 @@ def main():
     outs = (torch.empty(1, device=dev), torch.empty(N, device=dev), torch.empty(N, device=dev),
             torch.empty(N, D, device=dev, dtype=gdt), torch.empty(V, D, device=dev, dtype=gdt))
 
+    comp = torch.empty(V, D, device=dev, dtype=torch.bfloat16) if args.kahan else None
+
     def step(flags=0):
+        if args.kahan:
+            L.flce_fused_fwd_bwd_kahan(Hd, Wd, yd, reduction=wl.reduction,
+                                       filter_eps=args.filter_eps, flags=flags | flags0, ws=ws,
+                                       out=outs, dW_comp=comp)
+            return
         L.flce_fused_fwd_bwd(Hd, Wd, yd, reduction=wl.reduction, filter_eps=args.filter_eps,
                              flags=flags | flags0, ws=ws, out=outs)
 
@@ -518,6 +531,7 @@ def main():
                    "ignore_frac": wl.ignore_frac, "filter_eps": args.filter_eps,
                    "compact_ignored": bool(args.compact_ignored),
                    "grad_dtype": "bf16" if args.bf16_grads else "f32",
+                   "kahan_dW": bool(args.kahan),
                    "sort_vocab": bool(args.sort_vocab),
                    "parallelism": "single GPU"},
         "mfma_util": round(tflops / peak, 4), "tflops_counted_8ndv": round(tflops, 1),
@@ -525,7 +539,8 @@ def main():
         "peak_extra_mib": round(plan["ws_bytes"] / 2**20, 2),
         "torch_peak_alloc_delta_mib": round(peak_extra / 2**20, 2),
         "total_mib_incl_outputs": round((plan["ws_bytes"] + 4 * (2 * N + 1)
-                                         + (2 if args.bf16_grads else 4) * (N * D + V * D))
+                                         + (2 if args.bf16_grads else 4) * (N * D + V * D)
+                                         + (2 * V * D if args.kahan else 0))
                                         / 2**20, 1),
         "plan": {"band_rows": NS, "band_vocab": VS, "bands": n_bands,
                  "fwd_band_rows": plan["fwd_band_rows"], "fwd_workgroups": plan["fwd_workgroups"]},

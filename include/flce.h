@@ -221,6 +221,28 @@ int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const i
                        void* dH, void* dW,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* bf16 gradients with Kahan-compensated dW (CCE Sec. 5.1 and Table 1 rows
+ * 8-10, "CCE-Kahan": the gradient is summed in its final type with a
+ * compensation term of the same type).  Same arguments and results as
+ * flce_fused_fwd_bwd / flce_backward, plus dW_comp: a caller-owned device
+ * buffer of bf16 [V,D] (dW's layout, 16-byte aligned, outside the workspace,
+ * so the workspace bound is unchanged; CCE counts it in its memory column).
+ * desc->flags must hold FLCE_FLAG_BF16_GRADS, else FLCE_E_UNSUPPORTED; a NULL
+ * dW_comp is FLCE_E_NULL.  dH needs no compensation: it is summed in a float
+ * stage and rounded once.  dW of a vocabulary band is updated once per token
+ * band, each update in float: y = p - c, t = s + y, s <- bf16(t),
+ * c <- bf16((s_new - s) - y), with p the band's float partial and (s, c) the
+ * stored bf16 sum and compensation (the first band stores bf16(p) and the
+ * rounding it lost).  On return dW_comp holds the last compensation, with
+ * dW - dW_comp the closer estimate of the float sum; its contents on entry
+ * are ignored.  With one token band dW is bitwise the uncompensated result. */
+int flce_fused_fwd_bwd_kahan(const flce_desc* d, const void* H, const void* W, const int64_t* y,
+                             float* loss_rows, float* lse, float* loss, void* dH, void* dW,
+                             void* dW_comp, void* ws, size_t ws_bytes, hipStream_t stream);
+int flce_backward_kahan(const flce_desc* d, const void* H, const void* W, const int64_t* y,
+                        const float* lse, const float* dloss, void* dH, void* dW, void* dW_comp,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Multiplies dH [N,D] and dW [V,D] (in place, 16-byte aligned; float, or
  * bf16 under FLCE_FLAG_BF16_GRADS, rounded to nearest even) by the
  * upstream gradient dloss[0] (device pointer; NULL means 1: nothing to do).

@@ -31,6 +31,7 @@ from ._abi import (FLCE_BF16, FLCE_F32, FLCE_FLAG_BF16_GRADS, FLCE_FLAG_COMPACT_
                    FLCE_K_LSE_COMBINE, FLCE_MEAN, FLCE_NONE, FLCE_SUM, FlceError, lib)
 
 __all__ = ["flce_workspace_bytes", "flce_plan", "flce_forward", "flce_backward",
+           "flce_fused_fwd_bwd_kahan", "flce_backward_kahan",
            "flce_fused_fwd_bwd", "flce_scale_gradients", "flce_filter_stats", "flce_device_status",
            "flce_profile_reset", "flce_profile_read", "linear_cross_entropy", "Workspace", "FlceError", "lib",
            "FLCE_FLAG_PROFILE", "FLCE_FLAG_COMPACT_IGNORED", "FLCE_FLAG_BF16_GRADS",
@@ -198,6 +199,71 @@ def flce_fused_fwd_bwd(H, W, y, reduction="mean", ignore_index=-100, filter_eps=
     return loss, loss_rows, lse, dH, dW
 
 
+def _comp_for(W, dW_comp):
+    if dW_comp is None:
+        dW_comp = torch.empty(W.shape[0], W.shape[1], dtype=torch.bfloat16, device=W.device)
+    if dW_comp.dtype != torch.bfloat16 or tuple(dW_comp.shape) != tuple(W.shape) \
+            or not dW_comp.is_contiguous():
+        raise FlceError(_abi.FLCE_E_SHAPE, "dW_comp must be a contiguous bfloat16 tensor of W's shape")
+    return dW_comp
+
+
+def flce_fused_fwd_bwd_kahan(H, W, y, reduction="mean", ignore_index=-100, filter_eps=0.0,
+                             flags=FLCE_FLAG_BF16_GRADS, ws: Workspace | None = None,
+                             ws_budget_bytes=0, out=None, dW_comp=None):
+    """flce_fused_fwd_bwd with bf16 gradients and a Kahan-compensated dW; the
+    compensation buffer (bf16, W's shape) is allocated when not given.
+    Returns (loss, loss_rows, lse, dH, dW, dW_comp)."""
+    _check_inputs(H, W, y)
+    N, D = H.shape
+    V = W.shape[0]
+    d = make_desc(N, D, V, H.dtype, reduction, ignore_index, filter_eps, flags, ws_budget_bytes)
+    ws = _ws_for(d, H.device, ws)
+    dW_comp = _comp_for(W, dW_comp)
+    if out is None:
+        dev = H.device
+        loss = None if reduction == "none" else torch.empty(1, dtype=torch.float32, device=dev)
+        loss_rows = torch.empty(N, dtype=torch.float32, device=dev)
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        dH = torch.empty(N, D, dtype=_grad_dtype(flags), device=dev)
+        dW = torch.empty(V, D, dtype=_grad_dtype(flags), device=dev)
+    else:
+        loss, loss_rows, lse, dH, dW = out
+    _abi.check(lib().flce_fused_fwd_bwd_kahan(ctypes.byref(d), _ptr(H), _ptr(W), _ptr(y),
+                                              _ptr(loss_rows), _ptr(lse), _ptr(loss), _ptr(dH),
+                                              _ptr(dW), _ptr(dW_comp), ws.ptr(),
+                                              ctypes.c_size_t(ws.nbytes), _stream(H.device)))
+    return loss, loss_rows, lse, dH, dW, dW_comp
+
+
+def flce_backward_kahan(H, W, y, lse, dloss=None, reduction="mean", ignore_index=-100,
+                        filter_eps=0.0, flags=FLCE_FLAG_BF16_GRADS, ws: Workspace | None = None,
+                        ws_budget_bytes=0, out=None, dW_comp=None):
+    """flce_backward with bf16 gradients and a Kahan-compensated dW.
+    Returns (dH, dW, dW_comp)."""
+    _check_inputs(H, W, y)
+    N, D = H.shape
+    V = W.shape[0]
+    d = make_desc(N, D, V, H.dtype, reduction, ignore_index, filter_eps, flags, ws_budget_bytes)
+    ws = _ws_for(d, H.device, ws)
+    dW_comp = _comp_for(W, dW_comp)
+    if dloss is not None:
+        dloss = dloss.to(device=H.device, dtype=torch.float32).contiguous()
+        need = N if reduction == "none" else 1
+        if dloss.numel() != need:
+            raise FlceError(_abi.FLCE_E_SHAPE, f"dloss must have {need} elements")
+    if out is None:
+        dH = torch.empty(N, D, dtype=_grad_dtype(flags), device=H.device)
+        dW = torch.empty(V, D, dtype=_grad_dtype(flags), device=H.device)
+    else:
+        dH, dW = out
+    _abi.check(lib().flce_backward_kahan(ctypes.byref(d), _ptr(H), _ptr(W), _ptr(y), _ptr(lse),
+                                         _ptr(dloss), _ptr(dH), _ptr(dW), _ptr(dW_comp),
+                                         ws.ptr(), ctypes.c_size_t(ws.nbytes),
+                                         _stream(H.device)))
+    return dH, dW, dW_comp
+
+
 def flce_scale_gradients(dH, dW, dloss, reduction="mean", dtype=torch.bfloat16):
     """dH *= dloss[0], dW *= dloss[0] in place on the device (dloss: device float32
     [1], or None for 1); float32 or bfloat16 gradients (both the same type).
@@ -258,8 +324,12 @@ class _LinearCrossEntropy(torch.autograd.Function):
     def backward(ctx, g):
         H, W, y, lse = ctx.saved_tensors
         reduction, ignore_index, filter_eps, flags = ctx.cfg
-        dH, dW = flce_backward(H, W, y, lse, g.reshape(-1).float(), reduction, ignore_index,
-                               filter_eps, flags)
+        if flags & _KAHAN:
+            dH, dW, _ = flce_backward_kahan(H, W, y, lse, g.reshape(-1).float(), reduction,
+                                            ignore_index, filter_eps, flags & ~_KAHAN)
+        else:
+            dH, dW = flce_backward(H, W, y, lse, g.reshape(-1).float(), reduction, ignore_index,
+                                   filter_eps, flags)
         return dH.to(H.dtype), dW.to(W.dtype), None, None, None, None, None
 
 
@@ -271,8 +341,12 @@ class _LinearCrossEntropyGradsInForward(torch.autograd.Function):
     kept gradients are consumed by the first backward: a second one raises."""
     @staticmethod
     def forward(ctx, H, W, y, reduction, ignore_index, filter_eps, flags):
-        loss, _, _, dH, dW = flce_fused_fwd_bwd(H, W, y, reduction, ignore_index, filter_eps,
-                                                flags)
+        if flags & _KAHAN:
+            loss, _, _, dH, dW, _ = flce_fused_fwd_bwd_kahan(H, W, y, reduction, ignore_index,
+                                                             filter_eps, flags & ~_KAHAN)
+        else:
+            loss, _, _, dH, dW = flce_fused_fwd_bwd(H, W, y, reduction, ignore_index, filter_eps,
+                                                    flags)
         ctx.grads = (dH, dW)
         ctx.dtypes = (H.dtype, W.dtype, reduction)
         return loss.reshape(())
@@ -289,8 +363,12 @@ class _LinearCrossEntropyGradsInForward(torch.autograd.Function):
         return dH.to(h_dtype), dW.to(w_dtype), None, None, None, None, None
 
 
+# binding-side marker (not a library flag): take the Kahan-compensated entry points
+_KAHAN = 1 << 30
+
+
 def linear_cross_entropy(H, W, y, reduction="mean", ignore_index=-100, filter_eps=0.0,
-                         grads_in_forward=False, bf16_grads=False):
+                         grads_in_forward=False, bf16_grads=False, kahan=False):
     """loss = CE(H W^T, y) without materialising the logits (autograd-aware).
 
     grads_in_forward: for mean / sum, do all the contraction work (forward,
@@ -302,8 +380,15 @@ def linear_cross_entropy(H, W, y, reduction="mean", ignore_index=-100, filter_ep
     bf16_grads (bf16 inputs): the library writes dH and dW in bf16 directly
     (FLCE_FLAG_BF16_GRADS) instead of float32 that is then cast, so no float
     [V, D] gradient is ever allocated; dW takes one rounding per token band of
-    the backward plan instead of one."""
-    flags = FLCE_FLAG_BF16_GRADS if bf16_grads else 0
+    the backward plan instead of one.
+
+    kahan (with bf16_grads): dW's per-token-band updates carry a bf16
+    compensation term (CCE Sec. 5.1, "CCE-Kahan"), in a [V, D] bf16 buffer
+    allocated for the call, so dW ends within about one rounding of the float
+    sum."""
+    if kahan and not bf16_grads:
+        raise FlceError(_abi.FLCE_E_UNSUPPORTED, "kahan needs bf16_grads")
+    flags = (FLCE_FLAG_BF16_GRADS if bf16_grads else 0) | (_KAHAN if kahan else 0)
     if bf16_grads and H.dtype != torch.bfloat16:
         raise FlceError(_abi.FLCE_E_UNSUPPORTED, "bf16_grads needs bfloat16 inputs")
     if grads_in_forward and reduction != "none":

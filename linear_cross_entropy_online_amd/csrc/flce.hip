@@ -441,8 +441,9 @@ int run_sort(const flce_desc* d, const Plan& p, const void* H, const void* W, co
 }
 
 // One backward launch: grid = g_grad gradient tiles (the first g_long of the
-// contraction with the longer K) + the dZ tiles of `da`.
-template <typename T, bool BF16G>
+// contraction with the longer K) + the dZ tiles of `da`.  KAHAN: bf16 dW with
+// its compensation (bf16 gradients only).
+template <typename T, bool BF16G, bool KAHAN = false>
 void band_kernel(bool filt, bool compact, bool sort, dim3 grid, hipStream_t s,
                  const flce::GradArgs<T>& ga, const flce::DzArgs<T>& da, int g_long, int g_grad,
                  int h_first) {
@@ -450,29 +451,38 @@ void band_kernel(bool filt, bool compact, bool sort, dim3 grid, hipStream_t s,
   if constexpr (sizeof(T) == 2) {
     if (sort) {   // only with the filter
       if (compact)
-        flce::bwd_band_kernel<T, true, true, BF16G, true><<<grid, block, 0, s>>>(ga, da, g_long,
-                                                                                 g_grad, h_first);
+        flce::bwd_band_kernel<T, true, true, BF16G, true, KAHAN><<<grid, block, 0, s>>>(
+            ga, da, g_long, g_grad, h_first);
       else
-        flce::bwd_band_kernel<T, true, false, BF16G, true><<<grid, block, 0, s>>>(ga, da, g_long,
-                                                                                  g_grad, h_first);
+        flce::bwd_band_kernel<T, true, false, BF16G, true, KAHAN><<<grid, block, 0, s>>>(
+            ga, da, g_long, g_grad, h_first);
       return;
     }
     if (compact) {
       if (filt)
-        flce::bwd_band_kernel<T, true, true, BF16G><<<grid, block, 0, s>>>(ga, da, g_long, g_grad,
-                                                                           h_first);
+        flce::bwd_band_kernel<T, true, true, BF16G, false, KAHAN><<<grid, block, 0, s>>>(
+            ga, da, g_long, g_grad, h_first);
       else
-        flce::bwd_band_kernel<T, false, true, BF16G><<<grid, block, 0, s>>>(ga, da, g_long, g_grad,
-                                                                            h_first);
+        flce::bwd_band_kernel<T, false, true, BF16G, false, KAHAN><<<grid, block, 0, s>>>(
+            ga, da, g_long, g_grad, h_first);
       return;
     }
   }
-  if (filt)
-    flce::bwd_band_kernel<T, true, false, BF16G><<<grid, block, 0, s>>>(ga, da, g_long, g_grad,
-                                                                        h_first);
-  else
-    flce::bwd_band_kernel<T, false, false, BF16G><<<grid, block, 0, s>>>(ga, da, g_long, g_grad,
-                                                                         h_first);
+  if constexpr (!KAHAN) {
+    if (filt)
+      flce::bwd_band_kernel<T, true, false, BF16G><<<grid, block, 0, s>>>(ga, da, g_long, g_grad,
+                                                                          h_first);
+    else
+      flce::bwd_band_kernel<T, false, false, BF16G><<<grid, block, 0, s>>>(ga, da, g_long, g_grad,
+                                                                           h_first);
+  } else {
+    if (filt)
+      flce::bwd_band_kernel<T, true, false, BF16G, false, true><<<grid, block, 0, s>>>(
+          ga, da, g_long, g_grad, h_first);
+    else
+      flce::bwd_band_kernel<T, false, false, BF16G, false, true><<<grid, block, 0, s>>>(
+          ga, da, g_long, g_grad, h_first);
+  }
 }
 
 // The gradient filter's K-block counters in the workspace header.
@@ -494,7 +504,7 @@ unsigned long long* kblk_counters(const Ws& w) {
 template <typename T>
 int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, const int64_t* y,
               const float* lse, const float* dloss_rows, void* dH, void* dW, const Ws& w,
-              bool prof, hipStream_t s) {
+              bool prof, hipStream_t s, void* dWc = nullptr) {
   const int N = int(p.N), D = int(p.D), V = int(p.V);
   const int Td = int(cdiv(D, flce::kTile));
   const int nb = p.nbn * p.nbv;
@@ -536,7 +546,8 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
                              Td, bv > 0 ? 1 : 0, bn > 0 ? 1 : 0, skip_h, skip_w, w.rowmap, w.hdr,
                              p.bf16g ? static_cast<uint16_t*>(dH) : nullptr,
                              p.bf16g ? static_cast<uint16_t*>(dW) : nullptr, w.stage, h_mode,
-                             w.vperm, filt ? kblk_counters(w) : nullptr};
+                             static_cast<uint16_t*>(dWc), w.vperm,
+                             filt ? kblk_counters(w) : nullptr};
   };
   if (p.bf16g) {
     if constexpr (sizeof(T) == 2) {
@@ -549,8 +560,12 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
         int g_long = 0, g_grad = 0, h_first = 1;
         const flce::GradArgs<T> ga = grad_args(k, 0, g_long, g_grad, h_first);
         FLCE_TRY(launch(FLCE_K_BWD_GRAD, prof, s, [&] {
-          band_kernel<T, true>(filt, p.compact, p.sort, dim3(g_grad), s, ga, flce::DzArgs<T>{},
-                               g_long, g_grad, h_first);
+          if (dWc)
+            band_kernel<T, true, true>(filt, p.compact, p.sort, dim3(g_grad), s, ga,
+                                       flce::DzArgs<T>{}, g_long, g_grad, h_first);
+          else
+            band_kernel<T, true>(filt, p.compact, p.sort, dim3(g_grad), s, ga, flce::DzArgs<T>{},
+                                 g_long, g_grad, h_first);
         }));
       }
       return FLCE_OK;
@@ -595,6 +610,76 @@ int zero_dW(const Plan& p, void* dW, bool prof, hipStream_t s) {
     flce::fill_f32_kernel<<<dim3(1024), dim3(256), 0, s>>>(static_cast<float*>(dW),
                                                            p.V * p.D / (p.bf16g ? 2 : 1), 0.f);
   });
+}
+
+// Checks of a Kahan compensation buffer (bf16, dW's layout): only with bf16
+// gradients.
+int check_comp(const flce_desc* d, const void* dWc) {
+  if (!(d->flags & FLCE_FLAG_BF16_GRADS)) return FLCE_E_UNSUPPORTED;
+  if (!dWc) return FLCE_E_NULL;
+  if (!aligned(dWc, 16)) return FLCE_E_ALIGN;
+  return FLCE_OK;
+}
+
+// Forward then backward on the plan p for *d (argument checks, then the
+// launches); shared by the caller-workspace and compensated
+// entry points.  dWc: the bf16 compensation of dW, or null.
+int fused_with_plan(const flce_desc* d, const Plan& p, const void* H, const void* W,
+                    const int64_t* y, float* loss_rows, float* lse, float* loss, void* dH,
+                    void* dW, void* ws, size_t ws_bytes, hipStream_t stream,
+                    void* dWc = nullptr) {
+  FLCE_TRY(check_inputs(p, H, W, y));
+  if (p.N > 0 && (!loss_rows || !lse || !dH)) return FLCE_E_NULL;
+  if (!dW) return FLCE_E_NULL;
+  if (d->reduction != FLCE_NONE && !loss) return FLCE_E_NULL;
+  if (!aligned(dW, 16) || (dH && !aligned(dH, 16))) return FLCE_E_ALIGN;
+  FLCE_TRY(check_ws(p, ws, ws_bytes));
+  const bool prof = d->flags & FLCE_FLAG_PROFILE;
+  const Ws w = carve(p, ws);
+  if (p.N == 0) {
+    FLCE_TRY(launch(FLCE_K_AUX, prof, stream, [&] {
+      flce::clear_status_kernel<<<1, 64, 0, stream>>>(w.hdr, d->reduction != FLCE_NONE ? loss : nullptr);
+    }));
+    if (dWc) FLCE_TRY(zero_dW(p, dWc, prof, stream));
+    return zero_dW(p, dW, prof, stream);
+  }
+  if (p.compact) FLCE_TRY(run_compact(d, p, y, w, prof, stream));
+  if (p.dtype == FLCE_BF16) {
+    FLCE_TRY(run_forward<uint16_t>(d, p, H, W, y, loss_rows, lse, loss, w, prof, stream));
+    return run_bands<uint16_t>(d, p, H, W, y, lse, nullptr, dH, dW, w, prof, stream, dWc);
+  }
+  FLCE_TRY(run_forward<float>(d, p, H, W, y, loss_rows, lse, loss, w, prof, stream));
+  return run_bands<float>(d, p, H, W, y, lse, nullptr, dH, dW, w, prof, stream);
+}
+
+// Backward on the plan for *d; dWc as above.
+int backward_impl(const flce_desc* d, const void* H, const void* W, const int64_t* y,
+                  const float* lse, const float* dloss, void* dH, void* dW, void* ws,
+                  size_t ws_bytes, hipStream_t stream, void* dWc) {
+  Plan p;
+  FLCE_TRY(make_plan(d, p));
+  FLCE_TRY(check_inputs(p, H, W, y));
+  if (!dW || (p.N > 0 && (!dH || !lse))) return FLCE_E_NULL;
+  if (!aligned(dW, 16) || (dH && !aligned(dH, 16))) return FLCE_E_ALIGN;
+  FLCE_TRY(check_ws(p, ws, ws_bytes));
+  const bool prof = d->flags & FLCE_FLAG_PROFILE;
+  const Ws w = carve(p, ws);
+  if (p.N == 0) {
+    FLCE_TRY(launch(FLCE_K_AUX, prof, stream, [&] {
+      flce::clear_status_kernel<<<1, 64, 0, stream>>>(w.hdr, nullptr);
+    }));
+    if (dWc) FLCE_TRY(zero_dW(p, dWc, prof, stream));
+    return zero_dW(p, dW, prof, stream);
+  }
+  FLCE_TRY(launch(FLCE_K_FINALIZE, prof, stream, [&] {
+    flce::bwd_prep_kernel<<<dim3(1), dim3(256), 0, stream>>>(y, int(p.N), int(p.V), d->ignore_index,
+                                                             d->reduction, dloss, w.hdr);
+  }));
+  if (p.compact) FLCE_TRY(run_compact(d, p, y, w, prof, stream));
+  const float* drows = d->reduction == FLCE_NONE ? dloss : nullptr;
+  if (p.dtype == FLCE_BF16)
+    return run_bands<uint16_t>(d, p, H, W, y, lse, drows, dH, dW, w, prof, stream, dWc);
+  return run_bands<float>(d, p, H, W, y, lse, drows, dH, dW, w, prof, stream);
 }
 
 }  // namespace
@@ -650,29 +735,15 @@ int flce_forward(const flce_desc* d, const void* H, const void* W, const int64_t
 int flce_backward(const flce_desc* d, const void* H, const void* W, const int64_t* y,
                   const float* lse, const float* dloss, void* dH, void* dW, void* ws,
                   size_t ws_bytes, hipStream_t stream) {
-  Plan p;
-  FLCE_TRY(make_plan(d, p));
-  FLCE_TRY(check_inputs(p, H, W, y));
-  if (!dW || (p.N > 0 && (!dH || !lse))) return FLCE_E_NULL;
-  if (!aligned(dW, 16) || (dH && !aligned(dH, 16))) return FLCE_E_ALIGN;
-  FLCE_TRY(check_ws(p, ws, ws_bytes));
-  const bool prof = d->flags & FLCE_FLAG_PROFILE;
-  const Ws w = carve(p, ws);
-  if (p.N == 0) {
-    FLCE_TRY(launch(FLCE_K_AUX, prof, stream, [&] {
-      flce::clear_status_kernel<<<1, 64, 0, stream>>>(w.hdr, nullptr);
-    }));
-    return zero_dW(p, dW, prof, stream);
-  }
-  FLCE_TRY(launch(FLCE_K_FINALIZE, prof, stream, [&] {
-    flce::bwd_prep_kernel<<<dim3(1), dim3(256), 0, stream>>>(y, int(p.N), int(p.V), d->ignore_index,
-                                                             d->reduction, dloss, w.hdr);
-  }));
-  if (p.compact) FLCE_TRY(run_compact(d, p, y, w, prof, stream));
-  const float* drows = d->reduction == FLCE_NONE ? dloss : nullptr;
-  if (p.dtype == FLCE_BF16)
-    return run_bands<uint16_t>(d, p, H, W, y, lse, drows, dH, dW, w, prof, stream);
-  return run_bands<float>(d, p, H, W, y, lse, drows, dH, dW, w, prof, stream);
+  return backward_impl(d, H, W, y, lse, dloss, dH, dW, ws, ws_bytes, stream, nullptr);
+}
+
+int flce_backward_kahan(const flce_desc* d, const void* H, const void* W, const int64_t* y,
+                        const float* lse, const float* dloss, void* dH, void* dW, void* dW_comp,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  FLCE_TRY(validate(d));
+  FLCE_TRY(check_comp(d, dW_comp));
+  return backward_impl(d, H, W, y, lse, dloss, dH, dW, ws, ws_bytes, stream, dW_comp);
 }
 
 int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const int64_t* y,
@@ -680,27 +751,17 @@ int flce_fused_fwd_bwd(const flce_desc* d, const void* H, const void* W, const i
                        size_t ws_bytes, hipStream_t stream) {
   Plan p;
   FLCE_TRY(make_plan(d, p));
-  FLCE_TRY(check_inputs(p, H, W, y));
-  if (p.N > 0 && (!loss_rows || !lse || !dH)) return FLCE_E_NULL;
-  if (!dW) return FLCE_E_NULL;
-  if (d->reduction != FLCE_NONE && !loss) return FLCE_E_NULL;
-  if (!aligned(dW, 16) || (dH && !aligned(dH, 16))) return FLCE_E_ALIGN;
-  FLCE_TRY(check_ws(p, ws, ws_bytes));
-  const bool prof = d->flags & FLCE_FLAG_PROFILE;
-  const Ws w = carve(p, ws);
-  if (p.N == 0) {
-    FLCE_TRY(launch(FLCE_K_AUX, prof, stream, [&] {
-      flce::clear_status_kernel<<<1, 64, 0, stream>>>(w.hdr, d->reduction != FLCE_NONE ? loss : nullptr);
-    }));
-    return zero_dW(p, dW, prof, stream);
-  }
-  if (p.compact) FLCE_TRY(run_compact(d, p, y, w, prof, stream));
-  if (p.dtype == FLCE_BF16) {
-    FLCE_TRY(run_forward<uint16_t>(d, p, H, W, y, loss_rows, lse, loss, w, prof, stream));
-    return run_bands<uint16_t>(d, p, H, W, y, lse, nullptr, dH, dW, w, prof, stream);
-  }
-  FLCE_TRY(run_forward<float>(d, p, H, W, y, loss_rows, lse, loss, w, prof, stream));
-  return run_bands<float>(d, p, H, W, y, lse, nullptr, dH, dW, w, prof, stream);
+  return fused_with_plan(d, p, H, W, y, loss_rows, lse, loss, dH, dW, ws, ws_bytes, stream);
+}
+
+int flce_fused_fwd_bwd_kahan(const flce_desc* d, const void* H, const void* W, const int64_t* y,
+                             float* loss_rows, float* lse, float* loss, void* dH, void* dW,
+                             void* dW_comp, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Plan p;
+  FLCE_TRY(make_plan(d, p));
+  FLCE_TRY(check_comp(d, dW_comp));
+  return fused_with_plan(d, p, H, W, y, loss_rows, lse, loss, dH, dW, ws, ws_bytes, stream,
+                         dW_comp);
 }
 
 int flce_scale_gradients(const flce_desc* d, const float* dloss, void* dH, void* dW,

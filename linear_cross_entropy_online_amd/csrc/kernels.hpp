@@ -863,6 +863,7 @@ struct GradArgs {
   uint16_t* dWb;
   float* stage;
   int h_mode;
+  uint16_t* dWc;           // KAHAN: bf16 compensation of dWb, same layout
   const int* vperm;        // SORT: band vocabulary position p is row vperm[p] of W and dW
   unsigned long long* kblk;   // FILTER: Header::kblk (active, total K blocks), else null
 };
@@ -882,14 +883,23 @@ struct GradArgs {
 // previous batch's adds and stores.  bf16 values are widened exactly and
 // rounded to nearest even once.  Both contraction cores end with a barrier,
 // so the staging slots are free here.
-template <bool SRC_BF16, bool DST_BF16, bool SRC_MAPPED = false>
+//
+// KAHAN (bf16 source and destination only): the destination is a running
+// bf16 sum s with a bf16 compensation c of the same layout at rsC (Kahan's
+// compensated summation, CCE Sec. 5.1): with the tile's float partial p,
+// y = p - c, t = s + y, s' = bf16(t), c' = bf16((s' - s) - y), all in float,
+// so that s' - c' carries what the rounding of s' lost.  With src_on false
+// (first contribution) s = c = 0.
+template <bool SRC_BF16, bool DST_BF16, bool SRC_MAPPED = false, bool KAHAN = false>
 __device__ __forceinline__ void grad_epilogue_rows(const f32x16 (&acc)[4][4], bool src_on,
                                                    __amdgpu_buffer_rsrc_t rsS,
                                                    __amdgpu_buffer_rsrc_t rsD, const int* map,
                                                    int row0, int rvalid, int D, int td,
-                                                   char* lds) {
+                                                   char* lds, __amdgpu_buffer_rsrc_t rsC) {
+  static_assert(!KAHAN || (SRC_BF16 && DST_BF16), "compensation of a bf16 running sum");
   constexpr int SES = SRC_BF16 ? 2 : 4, DES = DST_BF16 ? 2 : 4;
-  constexpr int R = 16;   // rows of one batch
+  constexpr int R = KAHAN ? 8 : 16;   // rows of one batch
+  constexpr int NB = 64 / R;          // batches per wave (half a tile: 32 rows per wave)
   using Old = std::conditional_t<SRC_BF16, u32x2, f32x4>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -904,14 +914,19 @@ __device__ __forceinline__ void grad_epilogue_rows(const f32x16 (&acc)[4][4], bo
     const int r = (lane >> 5) * 128 + wave * 32 + (lane & 31);
     mapv = row0 + r < rvalid ? map[r] : 0;
   }
-  // batch n = 2 half + b: tile rows half * 128 + wave * 32 + b * R + k
-  auto issue = [&](int n, uint32_t (&od)[R], Old (&old)[R]) {
+  auto widen = [](u32x2 b) {   // four bf16 (element d in the low half of a dword)
+    return f32x4{__builtin_bit_cast(float, b[0] << 16), __builtin_bit_cast(float, b[0] & 0xffff0000u),
+                 __builtin_bit_cast(float, b[1] << 16), __builtin_bit_cast(float, b[1] & 0xffff0000u)};
+  };
+  // batch n: tile rows (n / (NB / 2)) * 128 + wave * 32 + (n % (NB / 2)) * R + k
+  auto issue = [&](int n, uint32_t (&od)[R], Old (&old)[R], u32x2 (&oc)[R]) {
 #pragma unroll
     for (int k = 0; k < R; ++k) {
-      const int trow = (n >> 1) * 128 + wave * 32 + (n & 1) * R + k;   // row within the tile
+      const int h = n / (NB / 2), b = n % (NB / 2);
+      const int trow = h * 128 + wave * 32 + b * R + k;   // row within the tile
       const bool rok = row0 + trow < rvalid, ok = rok && dok;
       const int64_t orow =
-          map ? (rok ? (int64_t)__builtin_amdgcn_readlane(mapv, (n >> 1) * 32 + (n & 1) * R + k) : 0)
+          map ? (rok ? (int64_t)__builtin_amdgcn_readlane(mapv, h * 32 + b * R + k) : 0)
               : trow;   // uniform per wave
       const uint32_t os = ok ? (uint32_t)(((SRC_MAPPED ? orow : (int64_t)trow) * D + dcol) * SES)
                              : kOob;
@@ -924,22 +939,39 @@ __device__ __forceinline__ void grad_epilogue_rows(const f32x16 (&acc)[4][4], bo
         old[k] = src_on ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                         rsS, os, 0, 0))
                         : f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (KAHAN)   // the compensation has the destination's layout
+        oc[k] = src_on ? __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                       rsC, od[k], 0, 0))
+                       : u32x2{0u, 0u};
     }
   };
-  auto finish = [&](int n, const uint32_t (&od)[R], const Old (&old)[R]) {
+  auto finish = [&](int n, const uint32_t (&od)[R], const Old (&old)[R], const u32x2 (&oc)[R]) {
 #pragma unroll
     for (int k = 0; k < R; ++k) {
-      const int rl = wave * 32 + (n & 1) * R + k;   // row within the half
+      const int rl = wave * 32 + (n % (NB / 2)) * R + k;   // row within the half
+      const f32x4 p = *reinterpret_cast<const f32x4*>(lds + rl * 1024 + ((lane ^ (rl & 31)) * 16));
+      if constexpr (KAHAN) {
+        const f32x4 s = widen(old[k]), c = widen(oc[k]);
+        u32x2 sb, cb;
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const float y0 = p[e] - c[e], y1 = p[e + 1] - c[e + 1];
+          const uint32_t t = pack_bf16x2(s[e] + y0, s[e + 1] + y1);
+          const float t0 = __builtin_bit_cast(float, t << 16);
+          const float t1 = __builtin_bit_cast(float, t & 0xffff0000u);
+          sb[e >> 1] = t;
+          cb[e >> 1] = pack_bf16x2((t0 - s[e]) - y0, (t1 - s[e + 1]) - y1);
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(sb, rsD, od[k], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(cb, rsC, od[k], 0, 0);
+        continue;
+      }
       f32x4 o;
-      if constexpr (SRC_BF16)   // element d in the low half of a dword
-        o = f32x4{__builtin_bit_cast(float, old[k][0] << 16),
-                  __builtin_bit_cast(float, old[k][0] & 0xffff0000u),
-                  __builtin_bit_cast(float, old[k][1] << 16),
-                  __builtin_bit_cast(float, old[k][1] & 0xffff0000u)};
+      if constexpr (SRC_BF16)
+        o = widen(old[k]);
       else
         o = old[k];
-      const f32x4 v =
-          *reinterpret_cast<const f32x4*>(lds + rl * 1024 + ((lane ^ (rl & 31)) * 16)) + o;
+      const f32x4 v = p + o;
       if constexpr (DST_BF16)
         __builtin_amdgcn_raw_buffer_store_b64(
             u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rsD, od[k], 0, 0);
@@ -966,17 +998,26 @@ __device__ __forceinline__ void grad_epilogue_rows(const f32x16 (&acc)[4][4], bo
   };
   uint32_t odA[R], odB[R];
   Old oldA[R], oldB[R];
-  issue(0, odA, oldA);
+  u32x2 ocA[R], ocB[R];   // compensation (KAHAN only; unused otherwise)
+  // batches 0 .. NB-1 with two in flight: the old values of batch n + 1 load
+  // while batch n is added and stored.  The first half's rows are staged
+  // after batch 0's loads are issued, the second half's once every wave has
+  // finished the first half (their loads already out).
+  issue(0, odA, oldA, ocA);
   stage(0);
-  issue(1, odB, oldB);
-  finish(0, odA, oldA);
-  issue(2, odA, oldA);
-  finish(1, odB, oldB);
-  __syncthreads();
-  stage(1);
-  issue(3, odB, oldB);
-  finish(2, odA, oldA);
-  finish(3, odB, oldB);
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    if (n + 1 < NB) {
+      if (n & 1) issue(n + 1, odA, oldA, ocA);
+      else issue(n + 1, odB, oldB, ocB);
+    }
+    if (n & 1) finish(n, odB, oldB, ocB);
+    else finish(n, odA, oldA, ocA);
+    if (n + 1 == NB / 2) {
+      __syncthreads();
+      stage(1);
+    }
+  }
   __syncthreads();
 }
 
@@ -989,8 +1030,10 @@ __device__ __forceinline__ void grad_epilogue_rows(const f32x16 (&acc)[4][4], bo
 // SORT: the band's vocabulary positions are rows vperm[p]: dH^T gathers W's
 // k rows through an LDS copy of the band's part of vperm, dW^T rows are
 // scattered through it.
-template <typename T, bool FILTER, bool COMPACT = false, bool BF16G = false, bool SORT = false>
+template <typename T, bool FILTER, bool COMPACT = false, bool BF16G = false, bool SORT = false,
+          bool KAHAN = false>
 __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int local, char* lds) {
+  static_assert(!KAHAN || BF16G, "the compensation is of bf16 gradients");
   const T* __restrict__ H = a.H;
   const T* __restrict__ W = a.W;
   const T* __restrict__ dz = a.dz;
@@ -1087,25 +1130,28 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
       const auto rsS = make_rsrc(reinterpret_cast<const char*>(a.stage + (int64_t)row0 * D));
       if (hm <= 1) {
         grad_epilogue_rows<false, false>(acc, hm == 1, rsS, rsS, nullptr, row0, rvalid, D, td,
-                                         lds);
+                                         lds, rsS);
       } else {
         // scattered rows: offsets from the start of dH (N D 4 < 2^31 with compaction)
         const auto rsD = make_rsrc(reinterpret_cast<const char*>(
             COMPACT ? a.dHb : a.dHb + ((int64_t)band.nb0 + row0) * D));
         grad_epilogue_rows<false, true>(acc, hm == 2, rsS, rsD,
                                         COMPACT ? a.rowmap + band.nb0 + row0 : nullptr, row0,
-                                        rvalid, D, td, lds);
+                                        rvalid, D, td, lds, rsD);
       }
     } else {
       if constexpr (SORT) {   // rows scattered: offsets from the start of dW (V D 4 < 2^31)
         const auto rs = make_rsrc(reinterpret_cast<const char*>(a.dWb));
-        grad_epilogue_rows<true, true, true>(acc, beta_w != 0, rs, rs, a.vperm + band.vb0 + row0,
-                                             row0, rvalid, D, td, lds);
+        const auto rc = make_rsrc(reinterpret_cast<const char*>(KAHAN ? a.dWc : a.dWb));
+        grad_epilogue_rows<true, true, true, KAHAN>(acc, beta_w != 0, rs, rs,
+                                                    a.vperm + band.vb0 + row0, row0, rvalid, D,
+                                                    td, lds, rc);
       } else {
-        const auto rs = make_rsrc(
-            reinterpret_cast<const char*>(a.dWb + ((int64_t)band.vb0 + row0) * D));
-        grad_epilogue_rows<true, true>(acc, beta_w != 0, rs, rs, nullptr, row0, rvalid, D, td,
-                                       lds);
+        const int64_t o = ((int64_t)band.vb0 + row0) * D;
+        const auto rs = make_rsrc(reinterpret_cast<const char*>(a.dWb + o));
+        const auto rc = make_rsrc(reinterpret_cast<const char*>((KAHAN ? a.dWc : a.dWb) + o));
+        grad_epilogue_rows<true, true, false, KAHAN>(acc, beta_w != 0, rs, rs, nullptr, row0,
+                                                     rvalid, D, td, lds, rc);
       }
     }
     return;
@@ -1172,7 +1218,8 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
     return;
   }
   // bf16 inputs: whole rows through LDS (old values at the out rows)
-  grad_epilogue_rows<false, false, true>(acc, beta != 0, rs, rs, smap, row0, rvalid, D, td, lds);
+  grad_epilogue_rows<false, false, true>(acc, beta != 0, rs, rs, smap, row0, rvalid, D, td, lds,
+                                         rs);
 }
 
 // One launch of the backward pipeline: the gradient tiles of band k - 1
@@ -1184,7 +1231,8 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
 // [g_grad, G) dZ tiles.
 constexpr int kBandLdsCompact = kDmaLdsBytes + 256 + kGatherTableBytes;   // slots, line touch, map
 
-template <typename T, bool FILTER, bool COMPACT, bool BF16G = false, bool SORT = false>
+template <typename T, bool FILTER, bool COMPACT, bool BF16G = false, bool SORT = false,
+          bool KAHAN = false>
 __global__ void __launch_bounds__(kThreads, 1)
 bwd_band_kernel(GradArgs<T> ga, DzArgs<T> da, int g_long, int g_grad, int h_first) {
   __shared__ __attribute__((aligned(1024))) char
@@ -1197,7 +1245,7 @@ bwd_band_kernel(GradArgs<T> ga, DzArgs<T> da, int g_long, int g_grad, int h_firs
   const int T3 = ga.Td * ga.T3n;   // dH^T tiles
   const bool is_h = h_first ? t < T3 : t >= g_long;
   const int local = h_first ? (is_h ? t : t - T3) : (is_h ? t - g_long : t);
-  grad_tile<T, FILTER, COMPACT, BF16G, SORT>(ga, is_h, local, lds);
+  grad_tile<T, FILTER, COMPACT, BF16G, SORT, KAHAN>(ga, is_h, local, lds);
 }
 
 }  // namespace flce

@@ -148,6 +148,17 @@ def test_argument_errors_return_before_any_device_work():
     tight = L.make_desc(8192, 2048, 151552, ws_budget_bytes=1 << 10)
     assert lib.flce_workspace_bytes(ctypes.byref(tight)) == 0
     assert lib.flce_scale_gradients(ctypes.byref(tight), None, ok[1], ok[2], None) == _abi.FLCE_OK
+    # Kahan-compensated calls: bf16 gradients only, a compensation buffer needed
+    assert lib.flce_fused_fwd_bwd_kahan(ctypes.byref(d), *ok[:3], ok[3], ok[4], ok[5], ok[0],
+                                        ok[1], ok[2], _fake(A), need, None) == \
+        _abi.FLCE_E_UNSUPPORTED
+    db = L.make_desc(8, 64, 10, flags=_abi.FLCE_FLAG_BF16_GRADS)
+    needb = lib.flce_workspace_bytes(ctypes.byref(db))
+    assert lib.flce_fused_fwd_bwd_kahan(ctypes.byref(db), *ok[:3], ok[3], ok[4], ok[5], ok[0],
+                                        ok[1], None, _fake(A), needb, None) == _abi.FLCE_E_NULL
+    assert lib.flce_backward_kahan(ctypes.byref(db), ok[0], ok[1], ok[2], ok[3], None, ok[4],
+                                   ok[5], _fake(A + 8), _fake(A), needb, None) == \
+        _abi.FLCE_E_ALIGN
     # fused: NULL workspace
     assert lib.flce_fused_fwd_bwd(ctypes.byref(d), *ok[:3], ok[3], ok[4], ok[5], ok[0], ok[1],
                                   None, need, None) == _abi.FLCE_E_NULL

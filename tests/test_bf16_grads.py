@@ -147,6 +147,79 @@ def test_bf16_grads_round_once_structure():
         assert float(eW.max()) <= 1.0
 
 
+def _kahan_bound(f32, TW, R, m):
+    """Bound on |Kahan-compensated bf16 dW - float dW| (reading r11): the
+    compensated sum s - c tracks the sum of the float band partials up to the
+    rounding of each stored compensation (|c| <= half a spacing of the running
+    sum, stored in bf16: at most 2^-9 of that, i.e. 2^-10 ulp of 1.2 T) and a
+    few float roundings per update (3 u T); the output s is within |c| <= half
+    a spacing of s - c; the float path's own sum is within gamma_m T."""
+    u = 2.0 ** -24
+    g = _gamma(m)
+    return (_ulp_bf16(f32.abs() + 2 * g * TW) / 2 + R * _ulp_bf16(1.2 * TW) / 1024
+            + (3 * R * u + 2 * g) * TW)
+
+
+@pytest.mark.parametrize("budget", [0, 1 << 20, 1 << 19])
+def test_kahan_dW_matches_oracle_and_stays_within_one_rounding(budget):
+    """Kahan-compensated bf16 dW (CCE Sec. 5.1): against the oracle at the bf16
+    tolerance; against the float path within the derived bound (about half a
+    spacing, not R/2); dH, the loss and the forward bitwise those of the
+    uncompensated bf16 path; with one token band dW too."""
+    N, D, V = 2100, 136, 3000
+    H, W, y = fi.random_case(N, D, V, seed=58, sigma_w=0.05, ignore_frac=0.05)
+    ref = O.linear_cross_entropy(H, W, y, reduction="mean")
+    TH, TW = _abs_terms(H, W, y)
+    Hd, Wd, yd = _dev(H, W, y)
+    plan = L.flce_plan(N, D, V, flags=B, ws_budget_bytes=budget)
+    R = plan["n_bands_rows"]
+    f = L.flce_fused_fwd_bwd(Hd, Wd, yd)
+    b = L.flce_fused_fwd_bwd(Hd, Wd, yd, flags=B, ws_budget_bytes=budget)
+    k = L.flce_fused_fwd_bwd_kahan(Hd, Wd, yd, ws_budget_bytes=budget)
+    _check(f"kahan_R{R}", k[:5], ref)
+    for i in range(4):
+        assert torch.equal(b[i], k[i])
+    if R == 1:
+        assert torch.equal(b[4], k[4])
+    dW32 = f[4].double().cpu()
+    bound = _kahan_bound(dW32, TW, R, N + R + 2)
+    e_k = float(((k[4].double().cpu() - dW32).abs() / bound).max())
+    ulp = _ulp_bf16(dW32)
+    report(f"kahan_R{R}", dW_of_bound=e_k,
+           kahan_max_ulps=float(((k[4].double().cpu() - dW32).abs() / ulp).max()),
+           plain_max_ulps=float(((b[4].double().cpu() - dW32).abs() / ulp).max()))
+    assert e_k <= 1.0
+
+
+def test_kahan_separate_backward_autograd_and_empty():
+    """The compensated backward (reduction none, per-row upstream gradients)
+    and the autograd paths against the oracle; N = 0 zeroes dW and the
+    compensation."""
+    N, D, V = 700, 128, 2100
+    H, W, y = fi.random_case(N, D, V, seed=59, sigma_w=0.08, ignore_frac=0.25)
+    g = torch.Generator().manual_seed(9)
+    dl = torch.randn(N, generator=g, dtype=torch.float64)
+    ref = O.linear_cross_entropy(H, W, y, reduction="none", dloss=dl.numpy())
+    Hd, Wd, yd = _dev(H, W, y)
+    loss, loss_rows, lse = L.flce_forward(Hd, Wd, yd, reduction="none")
+    dH, dW, _ = L.flce_backward_kahan(Hd, Wd, yd, lse, dl.float().to(DEV), reduction="none",
+                                      ws_budget_bytes=1 << 20)
+    _check("kahan_separate_none", (loss, loss_rows, lse, dH, dW), ref, "none")
+    ref = O.linear_cross_entropy(H, W, y, reduction="mean", dloss=0.5)
+    for gif in (False, True):
+        Hg, Wg = Hd.clone().requires_grad_(True), Wd.clone().requires_grad_(True)
+        out = L.linear_cross_entropy(Hg, Wg, yd, grads_in_forward=gif, bf16_grads=True, kahan=True)
+        (0.5 * out).backward()
+        vals = dict(dH=max_abs_rel(Hg.grad, ref["dH"]), dW=max_abs_rel(Wg.grad, ref["dW"]))
+        report(f"kahan_autograd_gif{int(gif)}", **vals)
+        assert vals["dH"] <= TOL["bf16"]["grad"] and vals["dW"] <= TOL["bf16"]["grad"]
+    He = torch.empty(0, D, dtype=torch.bfloat16, device=DEV)
+    ye = torch.empty(0, dtype=torch.int64, device=DEV)
+    comp = torch.full((V, D), 3.0, dtype=torch.bfloat16, device=DEV)
+    out = L.flce_fused_fwd_bwd_kahan(He, Wd, ye, dW_comp=comp)
+    assert out[0].item() == 0.0 and torch.all(out[4] == 0) and torch.all(comp == 0)
+
+
 @pytest.mark.parametrize("reduction", ["sum", "none"])
 def test_bf16_grads_separate_backward(reduction):
     H, W, y = fi.random_case(700, 128, 2100, seed=53, sigma_w=0.08, ignore_frac=0.25)

@@ -396,3 +396,14 @@ def test_long_context_bf16_grads(long_context):
     assert vals["loss"] <= tol["loss"]
     assert vals["dH"] <= tol["grad"] and vals["dW"] <= tol["grad"]
     assert ulps <= R / 2 + 1
+    # Kahan-compensated dW (CCE Sec. 5.1): the 32 roundings no longer add up;
+    # within about one spacing of the float path and the dH of the plain run
+    del b
+    k = L.flce_fused_fwd_bwd_kahan(Hd, Wd, yd, reduction="sum")
+    torch.cuda.synchronize()
+    kulps = float(((k[4].double() - dW32).abs() / unit).max())
+    vals = dict(dW=max_abs_rel(k[4][vs], dW_ref), dW_vs_float=max_abs_rel(k[4], dW32),
+                dW_ulps=kulps)
+    report("long_context_bf16_grads_kahan", **vals)
+    assert vals["dW"] <= tol["grad"]
+    assert kulps <= 1.0

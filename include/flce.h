@@ -243,6 +243,27 @@ int flce_backward_kahan(const flce_desc* d, const void* H, const void* W, const 
                         const float* lse, const float* dloss, void* dH, void* dW, void* dW_comp,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * forward + backward as flce_fused_fwd_bwd, with the same arguments minus the
+ * workspace.  The scratch is a 64 MiB device array inside the library, one
+ * per GPU, held until the process ends; its device address is looked up on
+ * the first call on each device (with that device current: it must be the
+ * stream's device), and no call allocates or frees anything.  The plan is
+ * made for a budget of min(desc->ws_budget_bytes or 64 MiB, 64 MiB), so at
+ * the default budget the launches and results are those of
+ * flce_fused_fwd_bwd bit for bit; a problem whose plan does not fit in 64 MiB
+ * returns FLCE_E_WORKSPACE (checked on the host before anything else).
+ * FLCE_FLAG_PROFILE is FLCE_E_UNSUPPORTED here (it creates events).  Every
+ * call on one GPU shares that GPU's array and leaves its contents behind
+ * (the next call needs no cleared scratch): two calls whose work overlaps on
+ * one GPU (other streams, other host threads) race and give wrong results;
+ * serialise them.  Other errors as flce_fused_fwd_bwd; FLCE_E_DEVICE if the
+ * array's address cannot be obtained. */
+int flce_fused_fwd_bwd_noalloc(const flce_desc* d, const void* H, const void* W,
+                               const int64_t* y, float* loss_rows, float* lse, float* loss,
+                               void* dH, void* dW, hipStream_t stream);
+
 /* Multiplies dH [N,D] and dW [V,D] (in place, 16-byte aligned; float, or
  * bf16 under FLCE_FLAG_BF16_GRADS, rounded to nearest even) by the
  * upstream gradient dloss[0] (device pointer; NULL means 1: nothing to do).

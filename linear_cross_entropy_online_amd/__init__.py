@@ -31,7 +31,7 @@ from ._abi import (FLCE_BF16, FLCE_F32, FLCE_FLAG_BF16_GRADS, FLCE_FLAG_COMPACT_
                    FLCE_K_LSE_COMBINE, FLCE_MEAN, FLCE_NONE, FLCE_SUM, FlceError, lib)
 
 __all__ = ["flce_workspace_bytes", "flce_plan", "flce_forward", "flce_backward",
-           "flce_fused_fwd_bwd_kahan", "flce_backward_kahan",
+           "flce_fused_fwd_bwd_noalloc", "flce_fused_fwd_bwd_kahan", "flce_backward_kahan",
            "flce_fused_fwd_bwd", "flce_scale_gradients", "flce_filter_stats", "flce_device_status",
            "flce_profile_reset", "flce_profile_read", "linear_cross_entropy", "Workspace", "FlceError", "lib",
            "FLCE_FLAG_PROFILE", "FLCE_FLAG_COMPACT_IGNORED", "FLCE_FLAG_BF16_GRADS",
@@ -262,6 +262,30 @@ def flce_backward_kahan(H, W, y, lse, dloss=None, reduction="mean", ignore_index
                                          ws.ptr(), ctypes.c_size_t(ws.nbytes),
                                          _stream(H.device)))
     return dH, dW, dW_comp
+
+
+def flce_fused_fwd_bwd_noalloc(H, W, y, reduction="mean", ignore_index=-100, filter_eps=0.0,
+                               flags=0, ws_budget_bytes=0, out=None):
+    """flce_fused_fwd_bwd on the library's static scratch array (no workspace
+    argument; the library allocates nothing).  Pass ``out`` to allocate
+    nothing here either.  Returns (loss, loss_rows, lse, dH, dW)."""
+    _check_inputs(H, W, y)
+    N, D = H.shape
+    V = W.shape[0]
+    d = make_desc(N, D, V, H.dtype, reduction, ignore_index, filter_eps, flags, ws_budget_bytes)
+    if out is None:
+        dev = H.device
+        loss = None if reduction == "none" else torch.empty(1, dtype=torch.float32, device=dev)
+        loss_rows = torch.empty(N, dtype=torch.float32, device=dev)
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        dH = torch.empty(N, D, dtype=_grad_dtype(flags), device=dev)
+        dW = torch.empty(V, D, dtype=_grad_dtype(flags), device=dev)
+    else:
+        loss, loss_rows, lse, dH, dW = out
+    _abi.check(lib().flce_fused_fwd_bwd_noalloc(ctypes.byref(d), _ptr(H), _ptr(W), _ptr(y),
+                                                _ptr(loss_rows), _ptr(lse), _ptr(loss), _ptr(dH),
+                                                _ptr(dW), _stream(H.device)))
+    return loss, loss_rows, lse, dH, dW
 
 
 def flce_scale_gradients(dH, dW, dloss, reduction="mean", dtype=torch.bfloat16):

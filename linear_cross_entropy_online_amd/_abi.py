@@ -22,7 +22,7 @@ FLCE_FLAG_SORT_VOCAB = 32
 
 # Every function include/flce.h declares (checked against the header by a CPU test).
 EXPORTS = ["flce_workspace_bytes", "flce_plan", "flce_forward", "flce_backward",
-           "flce_fused_fwd_bwd",
+           "flce_fused_fwd_bwd", "flce_fused_fwd_bwd_noalloc",
            "flce_fused_fwd_bwd_kahan", "flce_backward_kahan", "flce_scale_gradients", "flce_filter_stats", "flce_device_status",
            "flce_strerror",
            "flce_profile_reset", "flce_profile_read", "flce_version"]
@@ -78,6 +78,8 @@ def lib():
     L.flce_fused_fwd_bwd_kahan.restype = i32
     L.flce_backward_kahan.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.flce_backward_kahan.restype = i32
+    L.flce_fused_fwd_bwd_noalloc.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.flce_fused_fwd_bwd_noalloc.restype = i32
     L.flce_scale_gradients.argtypes = [pd, vp, vp, vp, vp]
     L.flce_scale_gradients.restype = i32
     L.flce_filter_stats.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int64),

@@ -33,6 +33,11 @@
 #include "kernels.hpp"
 #include "vocab_sort.hpp"
 
+// Device scratch of flce_fused_fwd_bwd_noalloc (64 MiB per GPU; see
+// scratch_of_current_device below for how host code reaches it).
+constexpr size_t kScratchBytes = 64ull << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 namespace {
 
 constexpr uint64_t kDefaultBudget = 64ull << 20;
@@ -622,7 +627,7 @@ int check_comp(const flce_desc* d, const void* dWc) {
 }
 
 // Forward then backward on the plan p for *d (argument checks, then the
-// launches); shared by the caller-workspace and compensated
+// launches); shared by the caller-workspace, static-scratch and compensated
 // entry points.  dWc: the bf16 compensation of dW, or null.
 int fused_with_plan(const flce_desc* d, const Plan& p, const void* H, const void* W,
                     const int64_t* y, float* loss_rows, float* lse, float* loss, void* dH,
@@ -680,6 +685,31 @@ int backward_impl(const flce_desc* d, const void* H, const void* W, const int64_
   if (p.dtype == FLCE_BF16)
     return run_bands<uint16_t>(d, p, H, W, y, lse, drows, dH, dW, w, prof, stream, dWc);
   return run_bands<float>(d, p, H, W, y, lse, drows, dH, dW, w, prof, stream);
+}
+
+// ------------------------------------------------ static scratch memory ----
+// The workspace of flce_fused_fwd_bwd_noalloc: a device array of the library
+// itself, one copy per GPU, held until the process ends.  Host code never
+// uses the array's name as an address (on the host it is a stand-in, not the
+// device copy): the device address is looked up once per device with that
+// device current and kept in g_scratch_ptr.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FLCE_E_DEVICE;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return FLCE_E_DEVICE;
+    if (!aligned(p, 256)) return FLCE_E_ALIGN;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FLCE_OK;
 }
 
 }  // namespace
@@ -762,6 +792,24 @@ int flce_fused_fwd_bwd_kahan(const flce_desc* d, const void* H, const void* W, c
   FLCE_TRY(check_comp(d, dW_comp));
   return fused_with_plan(d, p, H, W, y, loss_rows, lse, loss, dH, dW, ws, ws_bytes, stream,
                          dW_comp);
+}
+
+int flce_fused_fwd_bwd_noalloc(const flce_desc* d, const void* H, const void* W,
+                               const int64_t* y, float* loss_rows, float* lse, float* loss,
+                               void* dH, void* dW, hipStream_t stream) {
+  FLCE_TRY(validate(d));
+  // profiling creates HIP events: not for callers that cannot allocate
+  if (d->flags & FLCE_FLAG_PROFILE) return FLCE_E_UNSUPPORTED;
+  // the plan the caller's budget gives, held to the static scratch array
+  flce_desc dd = *d;
+  const uint64_t budget = d->ws_budget_bytes ? d->ws_budget_bytes : kDefaultBudget;
+  dd.ws_budget_bytes = std::min<uint64_t>(budget, kScratchBytes);
+  Plan p;
+  FLCE_TRY(make_plan(&dd, p));
+  if (p.total > kScratchBytes) return FLCE_E_WORKSPACE;
+  void* ws = nullptr;
+  FLCE_TRY(scratch_of_current_device(&ws));
+  return fused_with_plan(&dd, p, H, W, y, loss_rows, lse, loss, dH, dW, ws, kScratchBytes, stream);
 }
 
 int flce_scale_gradients(const flce_desc* d, const float* dloss, void* dH, void* dW,

@@ -148,6 +148,14 @@ def test_argument_errors_return_before_any_device_work():
     tight = L.make_desc(8192, 2048, 151552, ws_budget_bytes=1 << 10)
     assert lib.flce_workspace_bytes(ctypes.byref(tight)) == 0
     assert lib.flce_scale_gradients(ctypes.byref(tight), None, ok[1], ok[2], None) == _abi.FLCE_OK
+    # static-scratch fused call: a plan beyond the 64 MiB array is refused on
+    # the host, before the array's address is looked up
+    huge = L.make_desc((1 << 31) - 1, 64, 10)
+    assert lib.flce_fused_fwd_bwd_noalloc(ctypes.byref(huge), *ok[:3], ok[3], ok[4], ok[5],
+                                          ok[0], ok[1], None) == _abi.FLCE_E_WORKSPACE
+    prof = L.make_desc(8, 64, 10, flags=_abi.FLCE_FLAG_PROFILE)
+    assert lib.flce_fused_fwd_bwd_noalloc(ctypes.byref(prof), *ok[:3], ok[3], ok[4], ok[5],
+                                          ok[0], ok[1], None) == _abi.FLCE_E_UNSUPPORTED
     # Kahan-compensated calls: bf16 gradients only, a compensation buffer needed
     assert lib.flce_fused_fwd_bwd_kahan(ctypes.byref(d), *ok[:3], ok[3], ok[4], ok[5], ok[0],
                                         ok[1], ok[2], _fake(A), need, None) == \

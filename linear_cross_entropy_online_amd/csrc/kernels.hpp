@@ -46,6 +46,21 @@ static_assert(sizeof(Header) == 256, "the header is the first 256 bytes of the w
 // parity, i.e. 32 per 64-row filter block of the band.
 constexpr int kFilterHalfPerBlock = 32;
 
+// The bf16 core: four fragment sets and the barrier after a stage's second
+// sub-step (gemm_tile_dma2), except with a gathered A, whose row table and
+// per-lane indices leave no room for the two extra fragment sets (they
+// spill): two sets and the barrier before the last sub-step (gemm_tile_dma).
+template <bool AT, bool BT, class Active, bool GATHER_A>
+__device__ __forceinline__ void gemm_tile_dma_any(const Operand& A, const Operand& B, int m0,
+                                                  int n0, int nsteps, Active active,
+                                                  f32x16 (&acc)[4][4], char* lds, L2Split sa,
+                                                  L2Split sb) {
+  if constexpr (GATHER_A)
+    gemm_tile_dma<AT, BT, Active, GATHER_A>(A, B, m0, n0, nsteps, active, acc, lds, sa, sb);
+  else
+    gemm_tile_dma2<AT, BT, Active, GATHER_A>(A, B, m0, n0, nsteps, active, acc, lds, sa, sb);
+}
+
 // K elements of one pass of a tile contraction: 64 for bf16 (LDS-DMA core,
 // whole 128-byte lines per operand row), 32 for fp32 (register-staged core).
 template <typename T>
@@ -65,7 +80,7 @@ __device__ __forceinline__ void tile_contract(const Operand& A, const Operand& B
   // block is shared by 8 consecutive B tiles, a B block by 4 consecutive A
   // tiles, and consecutive tiles have distinct residues.
   if constexpr (sizeof(T) == 2)
-    gemm_tile_dma<AT, BT, Active, GATHER_A>(A, B, m0, n0, nsteps, active, acc, lds,
+    gemm_tile_dma_any<AT, BT, Active, GATHER_A>(A, B, m0, n0, nsteps, active, acc, lds,
                                              L2Split{(n0 / kTile) & 7, 8},
                                              L2Split{(m0 / kTile) & 3, 4});
   else gemm_tile<T, AT, BT>(A, B, m0, n0, nsteps, active, acc, lds);

@@ -25,9 +25,15 @@
 //    hardware hands lane i the element (row kbase + e, column mbase + i),
 //    e = 0..3, when source lane j points at row kbase + j / 4, columns
 //    mbase + 4 (j % 4) .. +3 (measured lane layout of the instruction).
-//  * One barrier per stage, before its last MFMA sub-step: the slot just
-//    read takes the DMAs of the stage after next, and the next stage's first
-//    fragments load while that sub-step runs.
+//  * One barrier per stage.  gemm_tile_dma2 (the default) reads all four
+//    sub-steps' fragments of a stage before its barrier, which sits after the
+//    second sub-step: the slot just read then takes the DMAs of the stage
+//    after next over the last two sub-steps, one instruction per MFMA pair,
+//    which is the rate the address unit drains them at (measured on MI355X:
+//    issuing them all in one sub-step stalls the MFMA issue; 8192^2 x 4096
+//    GEMM 1294 -> 1348 TFLOP/s).  gemm_tile_dma keeps two fragment sets and
+//    the barrier before the last sub-step, for callers with less register
+//    room.
 //  * Each workgroup also touches, one dword per 128-byte line, its share of
 //    the lines of the stage two ahead of the one being loaded, so those
 //    lines are in L2 when their DMAs are issued.
@@ -553,6 +559,134 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand& A, const Operand& B
   acc_fence(acc);
   wait_vmcnt<0>();   // DMAs past the last stage (out of range: zeros) and line touches
   __syncthreads();   // LDS may be reused by the caller
+}
+
+// One MFMA sub-step after a stage's barrier: eight steps of {DMA instruction
+// P of loader `ld` (the stage after next, into the slot just freed), one
+// fragment read of sub-step NKS of the next stage (A0, B0..B3, A1..A3), the
+// two MFMAs of blocks (P / 2, 2 (P % 2)) and (P / 2, 2 (P % 2) + 1)}.
+template <int P, int NKS, bool AT, bool BT, class LD>
+__device__ __forceinline__ void dma_substep(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
+                                            const bf16x8 (&b)[4], const LD& ld, uint32_t ld_op,
+                                            int k0, bool more, int wave,
+                                            __amdgpu_buffer_rsrc_t rs, const FragReader<AT>& fa,
+                                            const FragReader<BT>& fb, const char* sn,
+                                            bf16x8 (&an)[4], bf16x8 (&bn)[4]) {
+  if constexpr (P < 8) {
+    ld.template issue_q<P>(ld_op, k0, wave, more, rs);
+    if constexpr (P == 0) fa.template read_blk<NKS, 0>(sn, an);
+    else if constexpr (P <= 4) fb.template read_blk<NKS, P - 1>(sn + kDmaOpBytes, bn);
+    else fa.template read_blk<NKS, P - 4>(sn, an);
+    constexpr int i = P / 2, j = 2 * (P % 2);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    acc[i][j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j + 1], acc[i][j + 1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_substep<P + 1, NKS, AT, BT, LD>(acc, a, b, ld, ld_op, k0, more, wave, rs, fa, fb, sn, an,
+                                        bn);
+  }
+}
+
+// As gemm_tile_dma, with the stage's barrier after its second sub-step: the
+// fragments of all four sub-steps are read before it (four fragment sets,
+// one per sub-step), so the slot is free half a stage earlier and the DMAs of
+// the stage after next go out over two sub-steps (A's during the third, B's
+// during the fourth: one instruction per MFMA pair) instead of one.
+template <bool AT, bool BT, class Active, bool GATHER_A = false>
+__device__ __forceinline__ void gemm_tile_dma2(const Operand& A, const Operand& B, int m0, int n0,
+                                               int nsteps, Active active,
+                                               f32x16 (&acc)[4][4], char* lds,
+                                               L2Split sa = {0, 8}, L2Split sb = {0, 4}) {
+  static_assert(!GATHER_A || AT, "the gathered transposed loader is for a transposed A");
+  using LoaderA = std::conditional_t<GATHER_A, DmaTransposedGather, DmaLoader<AT>>;
+  active.prepare(nsteps);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int cur = active.next(0, nsteps);
+  if (cur >= nsteps) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    __syncthreads();
+    return;
+  }
+  int nxt = active.next(cur + 1, nsteps);
+  LoaderA la;
+  DmaLoader<BT> lb;
+  la.init(A, m0, wave, lane);
+  lb.init(B, n0, wave, lane);
+  FragReader<AT> fa;
+  FragReader<BT> fb;
+  fa.init(wm * 128, lane);
+  fb.init(wn * 128, lane);
+  const uint32_t lbase = lds_addr(lds);
+  auto issue = [&](int slot, int step) {
+    if constexpr (GATHER_A) la.rows(step * kDmaKStep);
+    la.issue(lbase + slot * kDmaStageBytes, step * kDmaKStep, wave);
+    lb.issue(lbase + slot * kDmaStageBytes + kDmaOpBytes, step * kDmaKStep, wave);
+  };
+  const uint32_t ldummy = lbase + kDmaLdsBytes;
+  auto prefetch = [&](int step) {
+    const bool on = step < nsteps;
+    if (wave == 1) lb.prefetch(ldummy, step * kDmaKStep, sb, lane, on);
+    else la.prefetch(ldummy, step * kDmaKStep, sa, lane, on && wave == 0);
+  };
+  constexpr int kReads = 4 * (AT ? 2 : 1) + 4 * (BT ? 2 : 1);
+  issue(0, cur);
+  if (nxt < nsteps) {
+    issue(1, nxt);
+    prefetch(nxt + 1);
+    prefetch(nxt + 2);
+    wait_vmcnt<18>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  barrier_raw();
+  bf16x8 a0[4], b0[4], a1[4], b1[4], a2[4], b2[4], a3[4], b3[4];
+  read_frags<0, AT, BT>(fa, fb, lds, a0, b0);
+  read_frags<1, AT, BT>(fa, fb, lds, a1, b1);
+  int slot = 0;
+  // one stage: ks0 and ks1 while ks2 / ks3 fragments load; barrier (this
+  // slot is then free); ks2 and ks3 while the DMAs of the stage after next
+  // fill this slot and the next stage's ks0 / ks1 fragments load
+  auto body = [&](auto fresh, bool& last) {
+    const char* s = lds + slot * kDmaStageBytes;
+    read_frags<2, AT, BT>(fa, fb, s, a2, b2);
+    mfma_group<decltype(fresh)::value>(acc, a0, b0);
+    interleave_reads_mfma<kReads>();
+    read_frags<3, AT, BT>(fa, fb, s, a3, b3);
+    mfma_group<false>(acc, a1, b1);
+    interleave_reads_mfma<kReads>();
+    last = nxt >= nsteps;
+    const int nn = last ? nsteps : active.next(nxt + 1, nsteps);
+    if constexpr (GATHER_A) la.rows((nn < nsteps ? nn : 0) * kDmaKStep);
+    wait_vmcnt<1>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier_raw();
+    if (last) return;
+    const bool more = nn < nsteps;
+    const int k0n = (more ? nn : 0) * kDmaKStep;
+    const uint32_t la_op = lbase + slot * kDmaStageBytes;
+    const char* sn = lds + (slot ^ 1) * kDmaStageBytes;
+    dma_substep<0, 0, AT, BT, LoaderA>(acc, a2, b2, la, la_op, k0n, more, wave, la.rsrc(k0n), fa,
+                                       fb, sn, a0, b0);
+    dma_substep<0, 1, AT, BT, DmaLoader<BT>>(acc, a3, b3, lb, la_op + kDmaOpBytes, k0n, more, wave,
+                                             lb.rsrc(k0n), fa, fb, sn, a1, b1);
+    prefetch(nn + 2);
+    nxt = nn;
+    slot ^= 1;
+  };
+  bool last = false;
+  body(std::true_type{}, last);
+  while (!last) body(std::false_type{}, last);
+  mfma_group<false>(acc, a2, b2);
+  mfma_group<false>(acc, a3, b3);
+  acc_fence(acc);
+  wait_vmcnt<0>();
+  __syncthreads();
 }
 
 }  // namespace flce

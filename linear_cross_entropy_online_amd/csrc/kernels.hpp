@@ -86,6 +86,10 @@ __device__ __forceinline__ void tile_contract(const Operand& A, const Operand& B
   else gemm_tile<T, AT, BT>(A, B, m0, n0, nsteps, active, acc, lds);
 }
 
+// The rescaled merges of (max, sum-exp) pairs below are written with explicit
+// fmaf: left to the compiler, a * b + c * d contracts to either fma(a, b, c d)
+// or fma(c, d, a b) depending on the surrounding code, which moved the last
+// bit of a sum between builds of the same source.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -168,7 +172,8 @@ fwd_lse_kernel(const T* __restrict__ H, const T* __restrict__ W,
     const float mo = __shfl_xor(m[j], 32), so = __shfl_xor(s[j], 32);
     const float M = fmaxf(m[j], mo);
     s[j] = (M == -INFINITY) ? 0.f
-                            : s[j] * fast_exp2((m[j] - M) * kLog2e) + so * fast_exp2((mo - M) * kLog2e);
+                            : fmaf(s[j], fast_exp2((m[j] - M) * kLog2e),
+                                   so * fast_exp2((mo - M) * kLog2e));
     m[j] = M;
   }
   if (wm == 1 && lane < 32) {
@@ -186,8 +191,8 @@ fwd_lse_kernel(const T* __restrict__ H, const T* __restrict__ W,
       const float mo = red[c * 2 + 0], so = red[c * 2 + 1];
       const float M = fmaxf(m[j], mo);
       const float S = (M == -INFINITY) ? 0.f
-                                       : s[j] * fast_exp2((m[j] - M) * kLog2e) +
-                                             so * fast_exp2((mo - M) * kLog2e);
+                                       : fmaf(s[j], fast_exp2((m[j] - M) * kLog2e),
+                                              so * fast_exp2((mo - M) * kLog2e));
       const int nl = tn * kTile + c;   // row within the band
       if (nl < ns) {
         part_m[(int64_t)tm * ns + nl] = M;
@@ -298,9 +303,9 @@ lse_combine_kernel(const float* __restrict__ part_m, const float* __restrict__ p
         const float m = mb[u], sk = sb[u];
         if (m == -INFINITY) continue;
         if (m <= M) {
-          S += sk * fast_exp2((m - M) * kLog2e);
+          S = fmaf(sk, fast_exp2((m - M) * kLog2e), S);
         } else {
-          S = S * fast_exp2((M - m) * kLog2e) + sk;   // M = -inf: S = 0 * 0 + sk
+          S = fmaf(S, fast_exp2((M - m) * kLog2e), sk);   // M = -inf: S = 0 * 0 + sk
           M = m;
         }
       }
@@ -321,7 +326,7 @@ lse_combine_kernel(const float* __restrict__ part_m, const float* __restrict__ p
     for (int q = 0; q < 16; ++q) Mx = fmaxf(Mx, sh_m[q][r]);
     float St = 0.f;
     for (int q = 0; q < 16; ++q)
-      St += sh_sum[q][r] * fast_exp2((sh_m[q][r] - Mx) * kLog2e);
+      St = fmaf(sh_sum[q][r], fast_exp2((sh_m[q][r] - Mx) * kLog2e), St);
     const float l = Mx + fast_log2(St) * kLn2;
     const int pos = nb0 + nl;                   // position (zy is by position)
     const int n = rowmap ? rowmap[pos] : pos;   // row

@@ -117,7 +117,7 @@ enum {
                                       is filtered ("FullE", Table 1 row 10),
                                       with a 64 x 256 filter block.  Setting
                                       both FULL flags is FLCE_E_UNSUPPORTED. */
-  FLCE_FLAG_SORT_VOCAB = 32u       /* with filter_eps > 0: the filter's
+  FLCE_FLAG_SORT_VOCAB = 32u,      /* with filter_eps > 0: the filter's
                                       vocabulary blocks are taken over the
                                       vocabulary ordered by decreasing average
                                       logit over the non-ignored rows (ties by
@@ -135,6 +135,19 @@ enum {
                                       flce_plan_info.vocab_order_offset, and
                                       its inverse).  No effect without the
                                       filter.                                */
+  FLCE_FLAG_WIDE_GRAD_TILES = 64u  /* keep every gradient contraction on
+                                      256 x 256 output tiles.  By default the
+                                      backward's last launch, which only
+                                      contracts, runs tiles 128 wide in d
+                                      when the band's 256 x 256 tiles would
+                                      fill at most half the CUs (small hidden
+                                      sizes; bf16 inputs with float gradients,
+                                      no compaction or sorted vocabulary;
+                                      flce_plan_info.grad_tile_d): the same
+                                      sums in the same order, so the results
+                                      are identical bit for bit; the flag
+                                      exists for comparison runs.  The
+                                      library's own option, not the pages'.  */
 };
 
 typedef struct flce_desc {
@@ -162,7 +175,8 @@ typedef struct flce_plan_info {
   int32_t n_bands_vocab;   /* ceil(V / VS)                                     */
   int32_t fwd_band_rows;   /* NF: token rows per forward band                  */
   int32_t fwd_workgroups;  /* forward grid of one band (256 x 256 logits tiles) */
-  int32_t tile;            /* output tile edge of every contraction (256)      */
+  int32_t tile;            /* output tile edge of every contraction (256; the
+                              gradient tiles' d width is grad_tile_d)         */
   int32_t filter_block;    /* edge of a filter block (64)                      */
   int64_t dz_bytes;        /* bytes of one staged dZ band buffer (two of them,
                               or one with FLCE_FLAG_BF16_GRADS)                */
@@ -170,6 +184,11 @@ typedef struct flce_plan_info {
                               offset in ws of the int32 [V] sorted vocabulary
                               (position -> vocabulary row) a backward leaves
                               there; else -1                                 */
+  int32_t grad_tile_d;     /* d width of the gradient tiles of the last
+                              backward launch: 256, or 128 (see
+                              FLCE_FLAG_WIDE_GRAD_TILES); the other launches
+                              use 256                                         */
+  int32_t reserved;        /* 0                                               */
 } flce_plan_info;
 
 /* Exact workspace size for *d (the maximum over the three compute entry

@@ -25,7 +25,7 @@ import torch
 from . import _abi
 from ._abi import (FLCE_BF16, FLCE_F32, FLCE_FLAG_BF16_GRADS, FLCE_FLAG_COMPACT_IGNORED,
                    FLCE_FLAG_FILTER_FULL_C, FLCE_FLAG_FILTER_FULL_E, FLCE_FLAG_PROFILE,
-                   FLCE_FLAG_SORT_VOCAB, FLCE_K_AUX,
+                   FLCE_FLAG_SORT_VOCAB, FLCE_FLAG_WIDE_GRAD_TILES, FLCE_K_AUX,
                    FLCE_K_BWD_BAND,
                    FLCE_K_BWD_DZ, FLCE_K_BWD_GRAD, FLCE_K_COUNT, FLCE_K_FINALIZE, FLCE_K_FWD_LSE,
                    FLCE_K_LSE_COMBINE, FLCE_MEAN, FLCE_NONE, FLCE_SUM, FlceError, lib)
@@ -36,6 +36,7 @@ __all__ = ["flce_workspace_bytes", "flce_plan", "flce_forward", "flce_backward",
            "flce_profile_reset", "flce_profile_read", "linear_cross_entropy", "Workspace", "FlceError", "lib",
            "FLCE_FLAG_PROFILE", "FLCE_FLAG_COMPACT_IGNORED", "FLCE_FLAG_BF16_GRADS",
            "FLCE_FLAG_FILTER_FULL_C", "FLCE_FLAG_FILTER_FULL_E", "FLCE_FLAG_SORT_VOCAB",
+           "FLCE_FLAG_WIDE_GRAD_TILES",
            "KERNEL_CLASSES"]
 
 _RED = {"mean": FLCE_MEAN, "sum": FLCE_SUM, "none": FLCE_NONE}

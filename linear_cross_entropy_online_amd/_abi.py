@@ -17,6 +17,7 @@ FLCE_FLAG_BF16_GRADS = 4
 FLCE_FLAG_FILTER_FULL_C = 8
 FLCE_FLAG_FILTER_FULL_E = 16
 FLCE_FLAG_SORT_VOCAB = 32
+FLCE_FLAG_WIDE_GRAD_TILES = 64
 (FLCE_K_FWD_LSE, FLCE_K_LSE_COMBINE, FLCE_K_FINALIZE, FLCE_K_BWD_DZ, FLCE_K_BWD_GRAD,
  FLCE_K_AUX, FLCE_K_BWD_BAND, FLCE_K_COUNT) = range(8)
 
@@ -41,7 +42,8 @@ class FlcePlanInfo(ctypes.Structure):
                 ("n_bands_vocab", ctypes.c_int32), ("fwd_band_rows", ctypes.c_int32),
                 ("fwd_workgroups", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("filter_block", ctypes.c_int32), ("dz_bytes", ctypes.c_int64),
-                ("vocab_order_offset", ctypes.c_int64)]
+                ("vocab_order_offset", ctypes.c_int64), ("grad_tile_d", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class FlceError(RuntimeError):

@@ -45,6 +45,8 @@ constexpr int kFilterBlock = 64;
 constexpr int kMaxBandRows = 4096;    // NS: token rows of a backward band
 constexpr int kMaxBandVocab = 8192;   // VS: the filter's K-skip masks cover K <= 8192
 constexpr int kMaxBandVocabSorted = 4096;   // VS with a sorted vocabulary: LDS row table
+constexpr int kCUs = 256;             // compute units of an MI355X (gfx950)
+constexpr int kNarrowTile = 128;      // d width of a narrow gradient tile
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -65,6 +67,7 @@ struct Plan {
   bool compact;        // ignored rows compacted away (row map in the workspace)
   bool bf16g;          // bf16 gradients: one dZ buffer + a float dH stage
   bool sort;           // sorted vocabulary (with the filter)
+  bool narrow;         // the last (gradient-only) launch runs tiles 128 wide in d
   int nsblk;           // radix-sort blocks
   size_t off_vperm, off_vinv, sort_bytes;
   int ncblk;           // compaction blocks
@@ -82,7 +85,7 @@ int validate(const flce_desc* d) {
   if (d->reduction < FLCE_MEAN || d->reduction > FLCE_NONE) return FLCE_E_UNSUPPORTED;
   constexpr uint32_t full = FLCE_FLAG_FILTER_FULL_C | FLCE_FLAG_FILTER_FULL_E;
   if (d->flags & ~uint32_t(FLCE_FLAG_PROFILE | FLCE_FLAG_COMPACT_IGNORED | FLCE_FLAG_BF16_GRADS |
-                           FLCE_FLAG_SORT_VOCAB | full))
+                           FLCE_FLAG_SORT_VOCAB | FLCE_FLAG_WIDE_GRAD_TILES | full))
     return FLCE_E_UNSUPPORTED;
   if ((d->flags & full) == full) return FLCE_E_UNSUPPORTED;
   if ((d->flags & FLCE_FLAG_BF16_GRADS) && d->in_dtype != FLCE_BF16) return FLCE_E_UNSUPPORTED;
@@ -248,6 +251,21 @@ int make_plan(const flce_desc* d, Plan& p) {
   p.nbf = int(cdiv(std::max<int64_t>(p.N, 1), p.NF));
   p.nbn = int(cdiv(std::max<int64_t>(p.N, 1), p.NS));
   p.nbv = int(cdiv(p.V, p.VS));
+  // The last launch only contracts (the gradient tiles of the last band).
+  // When a band's 256 x 256 gradient tiles would fill at most half the CUs
+  // (small hidden sizes: 128 tiles at 4096 x 1024 x 32000), that launch runs
+  // tiles 128 wide in d instead: twice the tiles, each with half the MFMA
+  // work, the same K order and sums (81 instead of 108 us there on MI355X).
+  // The pipelined launches keep 256 x 256: a 128-wide tile loads 3/4 of the
+  // operand bytes for 1/2 of the MFMAs, and the core's speed follows the LDS
+  // DMA bytes, so a narrow gradient tile beside a dZ tile ends later than a
+  // wide one (125 vs 115 us per launch).  bf16 inputs with float gradients,
+  // without compaction or a sorted vocabulary (their gathered loaders and
+  // scattered epilogues are 256 wide).
+  const int64_t wide_tiles =
+      cdiv(p.D, flce::kTile) * (cdiv(p.NS, flce::kTile) + cdiv(p.VS, flce::kTile));
+  p.narrow = p.dtype == FLCE_BF16 && !p.bf16g && !p.compact && !p.sort &&
+             !(d->flags & FLCE_FLAG_WIDE_GRAD_TILES) && 2 * wide_tiles <= kCUs;
   return FLCE_OK;
 }
 
@@ -449,10 +467,21 @@ int run_sort(const flce_desc* d, const Plan& p, const void* H, const void* W, co
 // contraction with the longer K) + the dZ tiles of `da`.  KAHAN: bf16 dW with
 // its compensation (bf16 gradients only).
 template <typename T, bool BF16G, bool KAHAN = false>
-void band_kernel(bool filt, bool compact, bool sort, dim3 grid, hipStream_t s,
+void band_kernel(bool filt, bool compact, bool sort, bool narrow, dim3 grid, hipStream_t s,
                  const flce::GradArgs<T>& ga, const flce::DzArgs<T>& da, int g_long, int g_grad,
                  int h_first) {
   const dim3 block(flce::kThreads);
+  if constexpr (sizeof(T) == 2 && !BF16G && !KAHAN) {
+    if (narrow) {   // 128-wide gradient tiles (no compaction or sorted vocabulary)
+      if (filt)
+        flce::bwd_band_kernel<T, true, false, false, false, false, true><<<grid, block, 0, s>>>(
+            ga, da, g_long, g_grad, h_first);
+      else
+        flce::bwd_band_kernel<T, false, false, false, false, false, true><<<grid, block, 0, s>>>(
+            ga, da, g_long, g_grad, h_first);
+      return;
+    }
+  }
   if constexpr (sizeof(T) == 2) {
     if (sort) {   // only with the filter
       if (compact)
@@ -511,7 +540,6 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
               const float* lse, const float* dloss_rows, void* dH, void* dW, const Ws& w,
               bool prof, hipStream_t s, void* dWc = nullptr) {
   const int N = int(p.N), D = int(p.D), V = int(p.V);
-  const int Td = int(cdiv(D, flce::kTile));
   const int nb = p.nbn * p.nbv;
   const bool filt = d->filter_eps > 0.f;
   // filter on one product only (CCE FullC / FullE): dZ keeps every value
@@ -534,8 +562,9 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
                            w.flagsT[buf], w.rowmap, keep_dropped, w.vperm, w.vinv};
   };
   // gradient tiles of band k reading buffer `buf`; g_long, g_grad, h_first out
-  auto grad_args = [&](int k, int buf, int& g_long, int& g_grad, int& h_first) {
+  auto grad_args = [&](int k, int buf, int& g_long, int& g_grad, int& h_first, bool narrow) {
     const flce::BandArgs band = band_args(p, k);
+    const int Td = int(cdiv(D, narrow ? kNarrowTile : flce::kTile));   // d tiles
     const int T2n = int(cdiv(band.vs_cur, flce::kTile));
     const int T3n = int(cdiv(band.ns_cur, flce::kTile));
     const int bn = k / p.nbv, bv = k % p.nbv;
@@ -559,17 +588,18 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
       for (int k = 0; k < nb; ++k) {
         const flce::DzArgs<T> da = dz_args(k, 0);
         FLCE_TRY(launch(FLCE_K_BWD_DZ, prof, s, [&] {
-          band_kernel<T, true>(filt, p.compact, p.sort, dim3(da.TMv * da.TNn), s,
+          band_kernel<T, true>(filt, p.compact, p.sort, false, dim3(da.TMv * da.TNn), s,
                                flce::GradArgs<T>{}, da, 0, 0, 1);
         }));
         int g_long = 0, g_grad = 0, h_first = 1;
-        const flce::GradArgs<T> ga = grad_args(k, 0, g_long, g_grad, h_first);
+        const flce::GradArgs<T> ga = grad_args(k, 0, g_long, g_grad, h_first, false);
         FLCE_TRY(launch(FLCE_K_BWD_GRAD, prof, s, [&] {
           if (dWc)
-            band_kernel<T, true, true>(filt, p.compact, p.sort, dim3(g_grad), s, ga,
+            band_kernel<T, true, true>(filt, p.compact, p.sort, false, dim3(g_grad), s, ga,
                                        flce::DzArgs<T>{}, g_long, g_grad, h_first);
           else
-            band_kernel<T, true>(filt, p.compact, p.sort, dim3(g_grad), s, ga, flce::DzArgs<T>{},
+            band_kernel<T, true>(filt, p.compact, p.sort, false, dim3(g_grad), s, ga,
+                                 flce::DzArgs<T>{},
                                  g_long, g_grad, h_first);
         }));
       }
@@ -585,11 +615,12 @@ int run_bands(const flce_desc* d, const Plan& p, const void* H, const void* W, c
       da = dz_args(k, k & 1);
       g_dz = da.TMv * da.TNn;
     }
-    if (k > 0) ga = grad_args(k - 1, (k - 1) & 1, g_long, g_grad, h_first);
+    const bool narrow = p.narrow && k == nb;   // the launch that only contracts
+    if (k > 0) ga = grad_args(k - 1, (k - 1) & 1, g_long, g_grad, h_first, narrow);
     const int cls = k == 0 ? FLCE_K_BWD_DZ : (k == nb ? FLCE_K_BWD_GRAD : FLCE_K_BWD_BAND);
     FLCE_TRY(launch(cls, prof, s, [&] {
-      band_kernel<T, false>(filt, p.compact, p.sort, dim3(g_grad + g_dz), s, ga, da, g_long,
-                            g_grad, h_first);
+      band_kernel<T, false>(filt, p.compact, p.sort, narrow, dim3(g_grad + g_dz), s, ga, da,
+                            g_long, g_grad, h_first);
     }));
   }
   return FLCE_OK;
@@ -737,6 +768,8 @@ int flce_plan(const flce_desc* d, flce_plan_info* out) {
   out->filter_block = kFilterBlock;
   out->dz_bytes = int64_t(p.NS) * p.VS * p.es;   // one dZ buffer
   out->vocab_order_offset = p.sort ? int64_t(p.off_vperm) : -1;
+  out->grad_tile_d = p.narrow ? kNarrowTile : flce::kTile;
+  out->reserved = 0;
   return FLCE_OK;
 }
 

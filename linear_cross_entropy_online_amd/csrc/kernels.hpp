@@ -1242,6 +1242,128 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
                                          rs);
 }
 
+// Epilogue of a 128 (d) x 256 (rows) gradient tile, float output:
+// out[r][d] = acc + out[r][d] (the old value only with src_on) for the tile
+// rows r < rvalid - row0 and d < D.  The whole tile goes through LDS as
+// [256 rows][512 B] (16-byte chunk c of row r at c ^ (r % 32)); then wave w
+// adds and stores rows 64 w .. 64 w + 63, a pair of whole rows per
+// instruction (lanes 0-31 the first, 32-63 the second), in four batches of
+// 16 rows whose old values load one batch ahead (the first batch's before
+// the accumulators are staged).
+__device__ __forceinline__ void grad_epilogue_narrow(const f32x16 (&acc)[2][4], bool src_on,
+                                                     __amdgpu_buffer_rsrc_t rs, int row0,
+                                                     int rvalid, int D, int td, char* lds) {
+  constexpr int R = 8;    // row pairs of one batch
+  constexpr int NB = 4;   // batches per wave
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ch = lane & 31, hr = lane >> 5;   // chunk of the row, row of the pair
+  const int dcol = td * 128 + ch * 4;
+  const bool dok = dcol < D;
+  auto issue = [&](int n, uint32_t (&od)[R], f32x4 (&old)[R]) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int r = 64 * wave + 2 * (n * R + k) + hr;
+      od[k] = row0 + r < rvalid && dok ? (uint32_t)(((int64_t)r * D + dcol) * 4) : kOob;
+      old[k] = src_on ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rs, od[k], 0, 0))
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto finish = [&](int n, const uint32_t (&od)[R], const f32x4 (&old)[R]) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int r = 64 * wave + 2 * (n * R + k) + hr;
+      const f32x4 p = *reinterpret_cast<const f32x4*>(lds + r * 512 + ((ch ^ (r & 31)) * 16));
+      const f32x4 v = p + old[k];
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, od[k], 0, 0);
+    }
+  };
+  uint32_t odA[R], odB[R];
+  f32x4 oldA[R], oldB[R];
+  issue(0, odA, oldA);
+  // acc[i][j][4q + e]: d = 64 wm + 32 i + 8 q + 4 (lane / 32) + e, row 128 wn + 32 j + lane % 32
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = wn * 128 + 32 * j + (lane & 31);
+        const int c = wm * 16 + 8 * i + 2 * q + (lane >> 5);
+        *reinterpret_cast<f32x4*>(lds + r * 512 + ((c ^ (r & 31)) * 16)) =
+            f32x4{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                  acc[i][j][4 * q + 3]};
+      }
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    if (n + 1 < NB) {
+      if (n & 1) issue(n + 1, odA, oldA);
+      else issue(n + 1, odB, oldB);
+    }
+    if (n & 1) finish(n, odB, oldB);
+    else finish(n, odA, oldA);
+  }
+  __syncthreads();
+}
+
+// Gradient tile `local` of a band's contraction (is_h: dH^T) as a 128 (d) x
+// 256 (rows) tile, bf16 inputs, float gradients, no compaction or vocabulary
+// order: the same products and K order as grad_tile, with d tiles of 128
+// (a.Td of them), for a launch that only contracts and would leave half the
+// CUs idle with 256-wide tiles.  FILTER: K steps skipped as in grad_tile.
+template <bool FILTER>
+__device__ __forceinline__ void grad_tile_narrow(const GradArgs<uint16_t>& a, bool is_h, int local,
+                                                 char* lds) {
+  const int D = a.D;
+  const BandArgs& band = a.band;
+  const int T3n = a.T3n, T2n = a.T2n, Td = a.Td;
+  f32x16 acc[2][4];
+  float* out;
+  int rvalid, beta, td, tr;
+  if (is_h) {
+    grouped_tile(local, Td, T3n, 4, td, tr);   // d tile, band row tile
+    out = a.dH + (int64_t)band.nb0 * D;
+    rvalid = band.ns_cur;
+    beta = a.beta_h;
+    const int kpad = min((band.vs_cur + kTile - 1) / kTile * kTile, band.ldz);
+    const Operand A{reinterpret_cast<const char*>(a.W + (int64_t)band.vb0 * D), D, D, band.vs_cur};
+    const Operand B{reinterpret_cast<const char*>(a.dz), band.ldz, (int64_t)T3n * kTile, kpad};
+    const int nsteps = (band.vs_cur + kDmaKStep - 1) / kDmaKStep;
+    if constexpr (FILTER) {
+      const SkipRowsOfFlags<kDmaKStep> act{a.flagsT + tr * 4, band.frows, !a.skip_h, 0, 0, a.kblk};
+      gemm_tile_dma2n<false>(A, B, td * 128, tr * kTile, nsteps, act, acc, lds,
+                             L2Split{tr & 7, 8}, L2Split{td & 3, 4});
+    } else {
+      gemm_tile_dma2n<false>(A, B, td * 128, tr * kTile, nsteps, AllActive{}, acc, lds,
+                             L2Split{tr & 7, 8}, L2Split{td & 3, 4});
+    }
+  } else {
+    grouped_tile(local, Td, T2n, 4, td, tr);   // d tile, band vocabulary tile
+    out = a.dW + (int64_t)band.vb0 * D;
+    rvalid = band.vs_cur;
+    beta = a.beta_w;
+    const Operand A{reinterpret_cast<const char*>(a.H + (int64_t)band.nb0 * D), D, D, band.ns_cur};
+    const Operand B{reinterpret_cast<const char*>(a.dz), band.ldz,
+                    min((int64_t)T2n * kTile, (int64_t)band.ldz), band.ns_cur};
+    const int nsteps = (band.ns_cur + kDmaKStep - 1) / kDmaKStep;
+    if constexpr (FILTER) {
+      const SkipRowsOfFlags<kDmaKStep> act{a.flags + tr * 4, band.fstride, !a.skip_w, 0, 0, a.kblk};
+      gemm_tile_dma2n<true>(A, B, td * 128, tr * kTile, nsteps, act, acc, lds,
+                            L2Split{tr & 7, 8}, L2Split{td & 3, 4});
+    } else {
+      gemm_tile_dma2n<true>(A, B, td * 128, tr * kTile, nsteps, AllActive{}, acc, lds,
+                            L2Split{tr & 7, 8}, L2Split{td & 3, 4});
+    }
+  }
+  const int row0 = tr * kTile;
+  grad_epilogue_narrow(acc, beta != 0,
+                       make_rsrc(reinterpret_cast<const char*>(out + (int64_t)row0 * D)), row0,
+                       rvalid, D, td, lds);
+}
+
 // One launch of the backward pipeline: the gradient tiles of band k - 1
 // (reading dZ buffer (k - 1) % 2) together with the dZ tiles of band k
 // (writing buffer k % 2), so that the tiles' memory-heavy epilogues do not
@@ -1252,7 +1374,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
 constexpr int kBandLdsCompact = kDmaLdsBytes + 256 + kGatherTableBytes;   // slots, line touch, map
 
 template <typename T, bool FILTER, bool COMPACT, bool BF16G = false, bool SORT = false,
-          bool KAHAN = false>
+          bool KAHAN = false, bool NARROW = false>
 __global__ void __launch_bounds__(kThreads, 1)
 bwd_band_kernel(GradArgs<T> ga, DzArgs<T> da, int g_long, int g_grad, int h_first) {
   __shared__ __attribute__((aligned(1024))) char
@@ -1265,7 +1387,12 @@ bwd_band_kernel(GradArgs<T> ga, DzArgs<T> da, int g_long, int g_grad, int h_firs
   const int T3 = ga.Td * ga.T3n;   // dH^T tiles
   const bool is_h = h_first ? t < T3 : t >= g_long;
   const int local = h_first ? (is_h ? t : t - T3) : (is_h ? t - g_long : t);
-  grad_tile<T, FILTER, COMPACT, BF16G, SORT, KAHAN>(ga, is_h, local, lds);
+  if constexpr (NARROW) {
+    static_assert(sizeof(T) == 2 && !COMPACT && !BF16G && !SORT, "128-wide gradient tiles");
+    grad_tile_narrow<FILTER>(ga, is_h, local, lds);
+  } else {
+    grad_tile<T, FILTER, COMPACT, BF16G, SORT, KAHAN>(ga, is_h, local, lds);
+  }
 }
 
 }  // namespace flce

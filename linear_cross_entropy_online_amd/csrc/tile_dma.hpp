@@ -689,6 +689,260 @@ __device__ __forceinline__ void gemm_tile_dma2(const Operand& A, const Operand& 
   __syncthreads();
 }
 
+// ------------------------------------------------- 128 x 256 tiles ----
+// A 128 (m) x 256 (n) output tile whose A operand is transposed ([k][m], M
+// contiguous) and 128 wide: the gradient contractions of a launch that only
+// contracts use it when 256 x 256 tiles would fill at most half the CUs (per
+// MFMA it loads 1.5 times the operand bytes, so it pays only where it puts
+// idle CUs to work).  Waves 2 x 2 as in the
+// 256 x 256 core, each holding 64 x 128 (acc[2][4]); the B side, the stage
+// slots and the schedule are those of gemm_tile_dma2.
+
+// The narrow A operand in LDS: [64 k rows][256 B], 32-byte segment s of row k
+// at s ^ (2 (k % 4)) (the wide layout's swizzle on a half-width row).  DMA
+// instruction q of wave w covers k rows 4 (4 w + q) .. +3 (1 KiB, two whole
+// 128-byte lines per row); lane L -> k row 4 (4 w + q) + L / 16, LDS 16-byte
+// chunk L % 16 of the row (segment (L % 16) / 2, half L % 2), global segment
+// ((L % 16) / 2) ^ (2 (L / 16)).
+struct DmaTransposedNarrow {
+  uint32_t off[4];
+  bool colok;             // this lane's 8 columns are inside the operand
+  const char* base;       // element (0, m0) of the stored [k][m] matrix
+  int64_t ld, kext, mrem;
+  int krow0;              // k row of instruction 0: 16 w + L / 16
+  __device__ __forceinline__ void init(const Operand& op, int m0, int wave, int lane) {
+    base = op.base + (int64_t)m0 * 2;
+    ld = op.ld;
+    kext = op.kext;
+    mrem = op.mext - m0;
+    krow0 = 16 * wave + (lane >> 4);
+    const int seg = ((lane & 15) >> 1) ^ (2 * (lane >> 4));   // k row % 4 = L / 16
+    const int m = seg * 16 + (lane & 1) * 8;
+    colok = (int64_t)m0 + m < op.mext;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) off[q] = (uint32_t)(((int64_t)(krow0 + 4 * q) * op.ld + m) * 2);
+  }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int k0) const {
+    return make_rsrc(base + (int64_t)k0 * ld * 2);
+  }
+  template <int Q>
+  __device__ __forceinline__ void issue_q(uint32_t lds_op, int k0, int wave, bool more,
+                                          __amdgpu_buffer_rsrc_t rs) const {
+    const bool ok = more && colok && (k0 + krow0 + 4 * Q < kext);
+    dma16(lds_op + (4 * wave + Q) * 1024, ok ? off[Q] : kOob, rs);
+  }
+  __device__ __forceinline__ void issue(uint32_t lds_op, int k0, int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(k0);
+    issue_q<0>(lds_op, k0, wave, true, rs);
+    issue_q<1>(lds_op, k0, wave, true, rs);
+    issue_q<2>(lds_op, k0, wave, true, rs);
+    issue_q<3>(lds_op, k0, wave, true, rs);
+  }
+  // two 128-byte lines per k row: lane L touches line li = share * per + L % per,
+  // k row li / 2, half li % 2
+  __device__ __forceinline__ void prefetch(uint32_t lds_dummy, int k0, L2Split sp, int lane,
+                                           bool on) const {
+    const int per = 128 / sp.nshare;
+    const int li = sp.share * per + (lane & (per - 1));
+    const int krow = li >> 1, half = li & 1;
+    const bool ok = on && k0 + krow < kext && half * 64 < mrem;
+    dma4(lds_dummy, ok ? (uint32_t)((int64_t)krow * ld * 2 + half * 128) : kOob, rsrc(k0));
+  }
+};
+
+// Fragments of the narrow A operand: as FragReader<true> on 256-byte rows,
+// two 32-column blocks per wave (wbase = 64 wm).
+struct FragReaderNarrow {
+  int addr[2];
+  __device__ __forceinline__ void init(int wbase, int lane) {
+    const int h = lane >> 5, g = (lane >> 4) & 1, j = lane & 15;
+    const int krow = 8 * h + (j >> 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int seg = (wbase >> 4) + 2 * i + g;
+      addr[i] = krow * 256 + ((seg ^ (2 * (krow & 3))) * 32) + (j & 3) * 8;
+    }
+  }
+  template <int KS, int I>
+  __device__ __forceinline__ void read_blk(const char* s, bf16x8 (&f)[2]) const {
+    lds_char* p = (lds_char*)(s + addr[I] + KS * 16 * 256);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 256));
+    f[I] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
+
+// Fragments of sub-step KS in the order the MFMA group uses them: A0, B0..B3, A1.
+template <int KS, bool BT>
+__device__ __forceinline__ void read_frags_n(const FragReaderNarrow& fa, const FragReader<BT>& fb,
+                                             const char* s, bf16x8 (&a)[2], bf16x8 (&b)[4]) {
+  fa.template read_blk<KS, 0>(s, a);
+  fb.template read_blk<KS, 0>(s + kDmaOpBytes, b);
+  fb.template read_blk<KS, 1>(s + kDmaOpBytes, b);
+  fb.template read_blk<KS, 2>(s + kDmaOpBytes, b);
+  fb.template read_blk<KS, 3>(s + kDmaOpBytes, b);
+  fa.template read_blk<KS, 1>(s, a);
+}
+
+// 4 x {R/4 LDS reads, 2 MFMA} for an 8-MFMA group.
+template <int R, int Q = 0>
+__device__ __forceinline__ void interleave_reads_mfma_n() {
+  if constexpr (Q < 4) {
+    constexpr int n = (R * (Q + 1)) / 4 - (R * Q) / 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, n, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+    interleave_reads_mfma_n<R, Q + 1>();
+  }
+}
+
+template <bool FRESH>
+__device__ __forceinline__ void mfma_group_n(f32x16 (&acc)[2][4], const bf16x8 (&a)[2],
+                                             const bf16x8 (&b)[4]) {
+  const f32x16 zero = {};
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], FRESH ? zero : acc[i][j],
+                                                          0, 0, 0);
+}
+
+// One MFMA sub-step after a stage's barrier (four pairs of MFMAs), with the
+// DMAs of the stage after next: NKS 0 issues A's four and B's first two,
+// NKS 1 B's other six (one or two per pair), and the fragment reads of
+// sub-step NKS of the next stage (A0 B0 | B1 | B2 | B3 A1).
+template <int P, int NKS, bool BT>
+__device__ __forceinline__ void dma_substep_n(f32x16 (&acc)[2][4], const bf16x8 (&a)[2],
+                                              const bf16x8 (&b)[4], const DmaTransposedNarrow& la,
+                                              const DmaLoader<BT>& lb, uint32_t la_op,
+                                              uint32_t lb_op, int k0, bool more, int wave,
+                                              __amdgpu_buffer_rsrc_t rsa,
+                                              __amdgpu_buffer_rsrc_t rsb,
+                                              const FragReaderNarrow& fa,
+                                              const FragReader<BT>& fb, const char* sn,
+                                              bf16x8 (&an)[2], bf16x8 (&bn)[4]) {
+  if constexpr (P < 4) {
+    if constexpr (NKS == 0) {
+      la.template issue_q<P>(la_op, k0, wave, more, rsa);
+      if constexpr (P < 2) lb.template issue_q<P>(lb_op, k0, wave, more, rsb);
+    } else {
+      lb.template issue_q<2 + P>(lb_op, k0, wave, more, rsb);
+      if constexpr (P < 2) lb.template issue_q<6 + P>(lb_op, k0, wave, more, rsb);
+    }
+    if constexpr (P == 0) {
+      fa.template read_blk<NKS, 0>(sn, an);
+      fb.template read_blk<NKS, 0>(sn + kDmaOpBytes, bn);
+    } else if constexpr (P < 3) {
+      fb.template read_blk<NKS, P>(sn + kDmaOpBytes, bn);
+    } else {
+      fb.template read_blk<NKS, 3>(sn + kDmaOpBytes, bn);
+      fa.template read_blk<NKS, 1>(sn, an);
+    }
+    constexpr int i = P / 2, j = 2 * (P % 2);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    acc[i][j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j + 1], acc[i][j + 1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_substep_n<P + 1, NKS, BT>(acc, a, b, la, lb, la_op, lb_op, k0, more, wave, rsa, rsb, fa,
+                                  fb, sn, an, bn);
+  }
+}
+
+// acc = sum over active K steps (64 wide) of A[m][k] B[n][k] for the
+// 128 x 256 tile at (m0, n0), A transposed and 128 wide; the stage schedule
+// of gemm_tile_dma2 (barrier after a stage's second sub-step, four fragment
+// sets, the DMAs of the stage after next over the last two sub-steps), with
+// 12 DMA instructions per wave and stage instead of 16.
+template <bool BT, class Active>
+__device__ __forceinline__ void gemm_tile_dma2n(const Operand& A, const Operand& B, int m0, int n0,
+                                                int nsteps, Active active, f32x16 (&acc)[2][4],
+                                                char* lds, L2Split sa, L2Split sb) {
+  active.prepare(nsteps);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int cur = active.next(0, nsteps);
+  if (cur >= nsteps) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    __syncthreads();
+    return;
+  }
+  int nxt = active.next(cur + 1, nsteps);
+  DmaTransposedNarrow la;
+  DmaLoader<BT> lb;
+  la.init(A, m0, wave, lane);
+  lb.init(B, n0, wave, lane);
+  FragReaderNarrow fa;
+  FragReader<BT> fb;
+  fa.init(wm * 64, lane);
+  fb.init(wn * 128, lane);
+  const uint32_t lbase = lds_addr(lds);
+  auto issue = [&](int slot, int step) {
+    la.issue(lbase + slot * kDmaStageBytes, step * kDmaKStep, wave);
+    lb.issue(lbase + slot * kDmaStageBytes + kDmaOpBytes, step * kDmaKStep, wave);
+  };
+  const uint32_t ldummy = lbase + kDmaLdsBytes;
+  auto prefetch = [&](int step) {
+    const bool on = step < nsteps;
+    if (wave == 1) lb.prefetch(ldummy, step * kDmaKStep, sb, lane, on);
+    else la.prefetch(ldummy, step * kDmaKStep, sa, lane, on && wave == 0);
+  };
+  constexpr int kReads = 2 * 2 + 4 * (BT ? 2 : 1);
+  issue(0, cur);
+  if (nxt < nsteps) {
+    issue(1, nxt);
+    prefetch(nxt + 1);
+    prefetch(nxt + 2);
+    wait_vmcnt<14>();      // the first stage (12 DMAs per wave per stage)
+  } else {
+    wait_vmcnt<0>();
+  }
+  barrier_raw();
+  bf16x8 a0[2], b0[4], a1[2], b1[4], a2[2], b2[4], a3[2], b3[4];
+  read_frags_n<0, BT>(fa, fb, lds, a0, b0);
+  read_frags_n<1, BT>(fa, fb, lds, a1, b1);
+  int slot = 0;
+  auto body = [&](auto fresh, bool& last) {
+    const char* s = lds + slot * kDmaStageBytes;
+    read_frags_n<2, BT>(fa, fb, s, a2, b2);
+    mfma_group_n<decltype(fresh)::value>(acc, a0, b0);
+    interleave_reads_mfma_n<kReads>();
+    read_frags_n<3, BT>(fa, fb, s, a3, b3);
+    mfma_group_n<false>(acc, a1, b1);
+    interleave_reads_mfma_n<kReads>();
+    last = nxt >= nsteps;
+    const int nn = last ? nsteps : active.next(nxt + 1, nsteps);
+    wait_vmcnt<1>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier_raw();
+    if (last) return;
+    const bool more = nn < nsteps;
+    const int k0n = (more ? nn : 0) * kDmaKStep;
+    const uint32_t la_op = lbase + slot * kDmaStageBytes;
+    const char* sn = lds + (slot ^ 1) * kDmaStageBytes;
+    const __amdgpu_buffer_rsrc_t rsa = la.rsrc(k0n), rsb = lb.rsrc(k0n);
+    dma_substep_n<0, 0, BT>(acc, a2, b2, la, lb, la_op, la_op + kDmaOpBytes, k0n, more, wave, rsa,
+                            rsb, fa, fb, sn, a0, b0);
+    dma_substep_n<0, 1, BT>(acc, a3, b3, la, lb, la_op, la_op + kDmaOpBytes, k0n, more, wave, rsa,
+                            rsb, fa, fb, sn, a1, b1);
+    prefetch(nn + 2);
+    nxt = nn;
+    slot ^= 1;
+  };
+  bool last = false;
+  body(std::true_type{}, last);
+  while (!last) body(std::false_type{}, last);
+  mfma_group_n<false>(acc, a2, b2);
+  mfma_group_n<false>(acc, a3, b3);
+  acc_fence(acc);
+  wait_vmcnt<0>();
+  __syncthreads();
+}
+
 }  // namespace flce
 
 #pragma clang diagnostic pop

@@ -283,6 +283,11 @@ __device__ __forceinline__ void acc_fence(f32x16 (&acc)[4][4]) {
                  "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
                  "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
 }
+__device__ __forceinline__ void acc_fence(f32x16 (&acc)[2][4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 1"
+               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                 "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]));
+}
 
 struct AllActive {
   __device__ __forceinline__ void prepare(int) {}

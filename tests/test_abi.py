@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import linear_cross_entropy_online_amd as L
 from linear_cross_entropy_online_amd import _abi
@@ -42,7 +43,8 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(_abi.FlceDesc) == 3 * 8 + 2 * 4 + 8 + 4 + 4 + 8
     assert _abi.FlceDesc.ignore_index.offset == 32
     assert _abi.FlceDesc.ws_budget_bytes.offset == 48
-    assert ctypes.sizeof(_abi.FlcePlanInfo) == 8 + 8 * 4 + 8 + 8
+    assert ctypes.sizeof(_abi.FlcePlanInfo) == 8 + 8 * 4 + 8 + 8 + 2 * 4
+    assert _abi.FlcePlanInfo.grad_tile_d.offset == 56
 
 
 def test_strerror_covers_codes():
@@ -70,7 +72,7 @@ def test_invalid_dtype_reduction_flags_eps():
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_DTYPE
     d = L.make_desc(8, 64, 10, reduction=5)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
-    d = L.make_desc(8, 64, 10, flags=64)
+    d = L.make_desc(8, 64, 10, flags=128)
     assert lib.flce_plan(ctypes.byref(d), ctypes.byref(info)) == _abi.FLCE_E_UNSUPPORTED
     # a filter on one product: C or E, not both
     d = L.make_desc(8, 64, 10, flags=_abi.FLCE_FLAG_FILTER_FULL_C | _abi.FLCE_FLAG_FILTER_FULL_E)
@@ -216,6 +218,31 @@ def test_plan_at_the_large_vocab_shape():
     assert L.flce_plan(8192, 2048, 151552, filter_eps=2.0 ** -12)["band_vocab"] == 4032
     one = L.flce_plan(8192, 2048, 151552, filter_eps=2.0 ** -12, flags=_abi.FLCE_FLAG_FILTER_FULL_C)
     assert one["band_vocab"] == 3840
+
+
+def test_gradient_tile_width():
+    """The last (gradient-only) launch runs 128-wide tiles exactly when a
+    band's 256 x 256 gradient tiles would fill at most half of the 256 CUs,
+    for bf16 inputs with float gradients and neither compaction nor a sorted
+    vocabulary; the flag keeps 256."""
+    mid = L.flce_plan(4096, 1024, 32000)
+    assert (mid["band_rows"], mid["band_vocab"]) == (4096, 4032)
+    assert mid["grad_tile_d"] == 128            # 4 x (16 + 16) = 128 tiles for 256 CUs
+    assert L.flce_plan(8192, 2048, 151552)["grad_tile_d"] == 256   # 8 x 32 = 256
+    assert L.flce_plan(4096, 1536, 32000)["grad_tile_d"] == 256    # 6 x 32 = 192 > 128
+    assert L.flce_plan(8192, 4096, 128256)["grad_tile_d"] == 256
+    assert L.flce_plan(4096, 1024, 32000, filter_eps=2.0 ** -12)["grad_tile_d"] == 128
+    for kw in ({"flags": _abi.FLCE_FLAG_WIDE_GRAD_TILES},
+               {"flags": _abi.FLCE_FLAG_BF16_GRADS},
+               {"flags": _abi.FLCE_FLAG_COMPACT_IGNORED},
+               {"flags": _abi.FLCE_FLAG_SORT_VOCAB, "filter_eps": 2.0 ** -12},
+               {"dtype": torch.float32}):
+        assert L.flce_plan(4096, 1024, 32000, **kw)["grad_tile_d"] == 256, kw
+    # small shapes: one d tile either way, 128 wide unless asked otherwise
+    assert L.flce_plan(700, 200, 3000)["grad_tile_d"] == 128
+    wide = L.flce_plan(700, 200, 3000, flags=_abi.FLCE_FLAG_WIDE_GRAD_TILES)
+    assert wide["grad_tile_d"] == 256
+    assert wide["ws_bytes"] == L.flce_plan(700, 200, 3000)["ws_bytes"]
 
 
 def test_bf16_gradient_plan_at_the_large_vocab_shape():

@@ -1323,8 +1323,12 @@ __device__ __forceinline__ void grad_tile_narrow(const GradArgs<uint16_t>& a, bo
   f32x16 acc[2][4];
   float* out;
   int rvalid, beta, td, tr;
+  // The filter's K-block counters count per 256-wide d range, as the wide
+  // tiles do: only the first of each pair of narrow tiles adds to them.
+  auto counters = [&](int t) { return (t & 1) ? nullptr : a.kblk; };
   if (is_h) {
     grouped_tile(local, Td, T3n, 4, td, tr);   // d tile, band row tile
+    unsigned long long* kblk = counters(td);
     out = a.dH + (int64_t)band.nb0 * D;
     rvalid = band.ns_cur;
     beta = a.beta_h;
@@ -1333,7 +1337,7 @@ __device__ __forceinline__ void grad_tile_narrow(const GradArgs<uint16_t>& a, bo
     const Operand B{reinterpret_cast<const char*>(a.dz), band.ldz, (int64_t)T3n * kTile, kpad};
     const int nsteps = (band.vs_cur + kDmaKStep - 1) / kDmaKStep;
     if constexpr (FILTER) {
-      const SkipRowsOfFlags<kDmaKStep> act{a.flagsT + tr * 4, band.frows, !a.skip_h, 0, 0, a.kblk};
+      const SkipRowsOfFlags<kDmaKStep> act{a.flagsT + tr * 4, band.frows, !a.skip_h, 0, 0, kblk};
       gemm_tile_dma2n<false>(A, B, td * 128, tr * kTile, nsteps, act, acc, lds,
                              L2Split{tr & 7, 8}, L2Split{td & 3, 4});
     } else {
@@ -1342,6 +1346,7 @@ __device__ __forceinline__ void grad_tile_narrow(const GradArgs<uint16_t>& a, bo
     }
   } else {
     grouped_tile(local, Td, T2n, 4, td, tr);   // d tile, band vocabulary tile
+    unsigned long long* kblk = counters(td);
     out = a.dW + (int64_t)band.vb0 * D;
     rvalid = band.vs_cur;
     beta = a.beta_w;
@@ -1350,7 +1355,7 @@ __device__ __forceinline__ void grad_tile_narrow(const GradArgs<uint16_t>& a, bo
                     min((int64_t)T2n * kTile, (int64_t)band.ldz), band.ns_cur};
     const int nsteps = (band.ns_cur + kDmaKStep - 1) / kDmaKStep;
     if constexpr (FILTER) {
-      const SkipRowsOfFlags<kDmaKStep> act{a.flags + tr * 4, band.fstride, !a.skip_w, 0, 0, a.kblk};
+      const SkipRowsOfFlags<kDmaKStep> act{a.flags + tr * 4, band.fstride, !a.skip_w, 0, 0, kblk};
       gemm_tile_dma2n<true>(A, B, td * 128, tr * kTile, nsteps, act, acc, lds,
                             L2Split{tr & 7, 8}, L2Split{td & 3, 4});
     } else {

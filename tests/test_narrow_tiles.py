@@ -65,12 +65,20 @@ def test_narrow_equals_wide_and_oracle(N, D, V, red, budget, seed):
 
 def test_narrow_filter_equals_wide():
     """Filter on both products (eps = 2^-12, 64 x 64 blocks): the narrow
-    tiles skip the same K steps as the wide ones."""
-    H, W, y = fi.random_case(640, 136, 19968, seed=84, sigma_w=0.4 / 136 ** 0.5)
+    tiles skip the same K steps as the wide ones, and the filter's K-block
+    counters (per 256-wide d range) read the same."""
+    N, D, V = 640, 392, 19968
+    H, W, y = fi.random_case(N, D, V, seed=84, sigma_w=0.4 / D ** 0.5)
     Hd, Wd, yd = H.to(DEV), W.to(DEV), y.to(DEV)
     eps = 2.0 ** -12
-    assert L.flce_plan(640, 136, 19968, filter_eps=eps)["grad_tile_d"] == 128
-    a = L.flce_fused_fwd_bwd(Hd, Wd, yd, filter_eps=eps)
-    b = L.flce_fused_fwd_bwd(Hd, Wd, yd, filter_eps=eps, flags=WIDE)
-    for x, z in zip(a, b):
+    assert L.flce_plan(N, D, V, filter_eps=eps)["grad_tile_d"] == 128
+    stats = []
+    outs = []
+    for flags in (0, WIDE):
+        ws = L.Workspace(L.flce_workspace_bytes(N, D, V, filter_eps=eps), DEV)
+        outs.append(L.flce_fused_fwd_bwd(Hd, Wd, yd, filter_eps=eps, flags=flags, ws=ws))
+        stats.append(L.flce_filter_stats(ws))
+    for x, z in zip(*outs):
         assert torch.equal(x, z)
+    report("narrow_filter", active=stats[0][0], total=stats[0][1])
+    assert stats[0] == stats[1] and 0 < stats[0][0] < stats[0][1]

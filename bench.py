@@ -28,7 +28,7 @@ PEAK_HBM_GBS = 8000.0
 SRC_DIR = os.path.join(ROOT, "linear_cross_entropy_online_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "bwd_band_8192x2048x151552_hbm_traffic.txt")
-DOMINANT = "bwd_band_kernel<unsigned short, false, false, false, false, false>"   # the backward launch of the default run
+DOMINANT = "bwd_band_kernel<unsigned short, false, false, false, false, false, false>"   # the backward launch of the default run
 
 
 def _code_only(text):

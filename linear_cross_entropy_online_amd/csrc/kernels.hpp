@@ -778,16 +778,24 @@ __device__ __forceinline__ void dz_tile(const DzArgs<T>& a, int t, char* lds) {
     // The tile's 128 KiB of bf16 dZ from LDS to the band: wave w stores rows
     // 64 w .. 64 w + 63, two whole 512-byte rows per instruction.  The band's
     // row stride is a multiple of 64 columns, not necessarily of the tile:
-    // 16-byte chunks past it belong to the next row and are not written.
+    // 16-byte chunks past it belong to the next row and are not written
+    // (their offset is out of range).  The stores are system-scope (sc0 sc1:
+    // written through rather than held dirty in this XCD's L2); the band is
+    // read in the next launch, after the launch boundary's cache write-back
+    // anyway, and the fused step is ~0.5% faster (17.56 -> 17.47 ms, same-box
+    // A/B at 8192 x 2048 x 151552).
     __syncthreads();
     const int half = lane >> 5, ch = lane & 31;
     T* base = dz + (int64_t)(n0 - band.nb0) * band.ldz + (v0 - band.vb0);
     const bool cin = (v0 - band.vb0) + ch * 8 < band.ldz;
+    const auto rsz = make_rsrc(reinterpret_cast<const char*>(base));
+    constexpr int kSc0Sc1 = 17;   // cache-policy bits of the buffer store: sc0 | sc1
 #pragma unroll 8
     for (int s2 = 0; s2 < 32; ++s2) {
       const int r = 64 * wave + 2 * s2 + half;
       const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * 512 + ((ch ^ (r & 31)) * 16));
-      if (cin) *reinterpret_cast<u32x4*>(base + (int64_t)r * band.ldz + ch * 8) = v;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          v, rsz, cin ? (uint32_t)(((int64_t)r * band.ldz + ch * 8) * 2) : kOob, 0, kSc0Sc1);
     }
   }
 }

@@ -956,21 +956,21 @@ __device__ __forceinline__ void grad_epilogue_rows(const f32x16 (&acc)[4][4], bo
       const int64_t orow =
           map ? (rok ? (int64_t)__builtin_amdgcn_readlane(mapv, h * 32 + b * R + k) : 0)
               : trow;   // uniform per wave
-      const uint32_t os = ok ? (uint32_t)(((SRC_MAPPED ? orow : (int64_t)trow) * D + dcol) * SES)
-                             : kOob;
+      // without a source every load is out of range and reads zeros: the loads
+      // are issued either way, so no branch sits between them and their uses
+      // (a branch per load made the wait before the first add cover the next
+      // batch's loads too)
+      const uint32_t os = ok && src_on
+                              ? (uint32_t)(((SRC_MAPPED ? orow : (int64_t)trow) * D + dcol) * SES)
+                              : kOob;
       od[k] = ok ? (uint32_t)((orow * D + dcol) * DES) : kOob;
       if constexpr (SRC_BF16)
-        old[k] = src_on ? __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                        rsS, os, 0, 0))
-                        : u32x2{0u, 0u};
+        old[k] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsS, os, 0, 0));
       else
-        old[k] = src_on ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                        rsS, os, 0, 0))
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
+        old[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsS, os, 0, 0));
       if constexpr (KAHAN)   // the compensation has the destination's layout
-        oc[k] = src_on ? __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                       rsC, od[k], 0, 0))
-                       : u32x2{0u, 0u};
+        oc[k] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsC, src_on ? od[k] : kOob, 0, 0));
     }
   };
   auto finish = [&](int n, const uint32_t (&od)[R], const Old (&old)[R], const u32x2 (&oc)[R]) {
@@ -1214,9 +1214,8 @@ __device__ __forceinline__ void grad_tile(const GradArgs<T>& a, bool is_h, int l
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          old[i][q] = beta ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                           rs, off[i][q], 0, 0))
-                           : f32x4{0.f, 0.f, 0.f, 0.f};
+          old[i][q] = __builtin_bit_cast(   // out of range (zeros) without beta
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, beta ? off[i][q] : kOob, 0, 0));
     };
     auto store = [&](int j, const uint32_t (&off)[4][4], const f32x4 (&old)[4][4]) {
 #pragma unroll
@@ -1274,9 +1273,9 @@ __device__ __forceinline__ void grad_epilogue_narrow(const f32x16 (&acc)[2][4], 
     for (int k = 0; k < R; ++k) {
       const int r = 64 * wave + 2 * (n * R + k) + hr;
       od[k] = row0 + r < rvalid && dok ? (uint32_t)(((int64_t)r * D + dcol) * 4) : kOob;
-      old[k] = src_on ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      rs, od[k], 0, 0))
-                      : f32x4{0.f, 0.f, 0.f, 0.f};
+      // branch-free: without a source the load is out of range and reads zeros
+      old[k] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, src_on ? od[k] : kOob, 0, 0));
     }
   };
   auto finish = [&](int n, const uint32_t (&od)[R], const f32x4 (&old)[R]) {

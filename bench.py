@@ -383,7 +383,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path's sharding is described in DESIGN.md)", file=sys.stderr)
+              "(sharding the path over several GPUs is designed, not built)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -35,7 +35,7 @@ What it computes, and where the pages define it
   vocabulary blocks are taken over that order instead of the natural one,
   so that entries with non-trivial gradients share blocks.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 * LSE is produced for every row, ignored ones included.
 * The filter decision uses the unscaled G of non-ignored rows only; a block
   with no non-ignored row is dropped (its dZ is zero either way).

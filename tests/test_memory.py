@@ -1,5 +1,5 @@
-"""Extra device memory of a call (SURVEY's T7; PyTorch 2.13 chapter, section
-on measuring peak memory): with inputs, outputs and the workspace allocated
+"""Extra device memory of a call (PyTorch 2.13 chapter, section on measuring
+peak memory): with inputs, outputs and the workspace allocated
 beforehand, a fused call allocates nothing (torch's allocator peak does not
 move and the device's free memory is unchanged), and the workspace it needs
 at 8192 x 2048 x 151552 is within 64 MiB for every flag combination."""

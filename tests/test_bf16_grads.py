@@ -112,7 +112,7 @@ def _gamma(m):
 def test_bf16_grads_round_once_structure():
     """dH is the float sum rounded once, dW is rounded once per token band;
     checked against the library's own float path with bounds derived from the
-    arithmetic (reading r11).  Both paths sum the same bf16 dZ terms (the
+    arithmetic.  Both paths sum the same bf16 dZ terms (the
     forward and the dZ tiles are the same kernels: checked bitwise below) in
     float32, in different orders, so their float sums S_b, S_f each lie within
     gamma_m T of the exact sum, T = sum of |terms| of the entry and m the
@@ -148,7 +148,7 @@ def test_bf16_grads_round_once_structure():
 
 
 def _kahan_bound(f32, TW, R, m):
-    """Bound on |Kahan-compensated bf16 dW - float dW| (reading r11): the
+    """Bound on |Kahan-compensated bf16 dW - float dW|: the
     compensated sum s - c tracks the sum of the float band partials up to the
     rounding of each stored compensation (|c| <= half a spacing of the running
     sum, stored in bf16: at most 2^-9 of that, i.e. 2^-10 ulp of 1.2 T) and a
